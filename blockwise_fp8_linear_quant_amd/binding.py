@@ -1,0 +1,166 @@
+"""Thin Python binding over the C ABI of libfp8blk.so.
+
+Functions carry the C names.  They only marshal arguments: torch tensors
+provide device memory, `torch.cuda.current_stream()` provides the stream, and
+every step of the computation runs in the HIP kernels behind the C ABI.
+Outputs the caller does not pass in are allocated with torch.
+
+Layouts (see include/fp8blk.h for the full contract):
+  row-wise codes  q [R, C] uint8, scales [ceil(C/128), R] float32 (group-major)
+  token-dim codes qT [C, round_up(M,128)] uint8, scales [ceil(M/128), C] float32
+  block codes     q [R, C] uint8, scales [ceil(R/128), ceil(C/128)] float32
+Scale tensors may be row-strided views (leading dimension padded to a multiple
+of 4 floats so that the GEMMs can read them with 16-byte loads).
+"""
+
+import torch
+
+from . import _lib
+
+OUT_F32 = 0
+OUT_BF16 = 1
+
+
+def _stream(t):
+    return ctypes_stream(torch.cuda.current_stream(t.device))
+
+
+def ctypes_stream(s):
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _round_up(a, b):
+    return (a + b - 1) // b * b
+
+
+def _check_2d(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a 2-D {dtype} CUDA tensor")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+
+
+def _scales(rows, cols, device):
+    """float32 [rows, cols] view of a buffer whose leading dimension is a multiple of 4."""
+    ld = _round_up(max(cols, 1), 4)
+    return torch.empty((rows, ld), dtype=torch.float32, device=device)[:, :cols]
+
+
+def fp8_quant_1x128(x, transpose_out=False, q=None, scales=None):
+    """1x128 group quantisation of BF16 x [rows, cols] -> (codes, scales)."""
+    _check_2d(x, torch.bfloat16, "x")
+    R, C = x.shape
+    if not transpose_out:
+        if q is None:
+            q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = _scales(-(-C // 128), R, x.device)
+    else:
+        if q is None:
+            q = torch.empty((C, _round_up(R, 128)), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = _scales(-(-R // 128), C, x.device)
+    st = _lib.load().fp8_quant_1x128(
+        _ptr(x), R, C, x.stride(0), 1 if transpose_out else 0,
+        _ptr(q), q.stride(0), _ptr(scales), scales.stride(0), _stream(x))
+    _lib.check(st, "fp8_quant_1x128")
+    return q, scales
+
+
+def fp8_quant_128x128(w, with_transpose=False, q=None, scales=None, qT=None, scalesT=None):
+    """128x128 block quantisation of BF16 w [rows, cols] -> (q, scales, qT, scalesT)."""
+    _check_2d(w, torch.bfloat16, "w")
+    R, C = w.shape
+    br, bc = -(-R // 128), -(-C // 128)
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((br, bc), dtype=torch.float32, device=w.device)
+    if with_transpose:
+        if qT is None:
+            qT = torch.empty((C, R), dtype=torch.uint8, device=w.device)
+        if scalesT is None:
+            scalesT = torch.empty((bc, br), dtype=torch.float32, device=w.device)
+    st = _lib.load().fp8_quant_128x128(
+        _ptr(w), R, C, w.stride(0), _ptr(q), q.stride(0), _ptr(scales),
+        _ptr(qT), qT.stride(0) if qT is not None else 0, _ptr(scalesT), _stream(w))
+    _lib.check(st, "fp8_quant_128x128")
+    return q, scales, qT, scalesT
+
+
+def _out(shape, out_dtype, device, y):
+    if y is not None:
+        return y
+    return torch.empty(shape, dtype=out_dtype, device=device)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return OUT_F32
+    if t.dtype == torch.bfloat16:
+        return OUT_BF16
+    raise TypeError("output must be float32 or bfloat16")
+
+
+def fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None):
+    """Y[M, N] = Xq . Wq^T with 1x128 row scales sx [K/128, M] and block scales sw [N/128, K/128]."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = _out((M, N), out_dtype, xq.device, y)
+    st = _lib.load().fp8_block_gemm_fwd(
+        _ptr(xq), xq.stride(0), _ptr(sx), sx.stride(0), _ptr(wq), wq.stride(0), _ptr(sw),
+        M, N, K, _ptr(y), y.stride(0), _dtype_code(y), None, 0, _stream(xq))
+    _lib.check(st, "fp8_block_gemm_fwd")
+    return y
+
+
+def fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, dx=None):
+    """dX[M, K] = dY . W from dYq [M, N] (row scales sdy [N/128, M]) and WqT [K, N] (scales swT [K/128, N/128])."""
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    dx = _out((M, K), out_dtype, dyq.device, dx)
+    st = _lib.load().fp8_block_gemm_dgrad(
+        _ptr(dyq), dyq.stride(0), _ptr(sdy), sdy.stride(0), _ptr(wqT), wqT.stride(0), _ptr(swT),
+        M, N, K, _ptr(dx), dx.stride(0), _dtype_code(dx), None, 0, _stream(dyq))
+    _lib.check(st, "fp8_block_gemm_dgrad")
+    return dx
+
+
+def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False):
+    """dW[N, K] (+)= dY^T . X from token-dimension codes dyqT [N, M_pad], xqT [K, M_pad]."""
+    N = dyqT.shape[0]
+    K = xqT.shape[0]
+    if M is None:
+        M = dyqT.shape[1]
+    if dw is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing dw")
+        dw = torch.empty((N, K), dtype=torch.float32, device=dyqT.device)
+    st = _lib.load().fp8_block_gemm_wgrad(
+        _ptr(dyqT), dyqT.stride(0), _ptr(sdyT), sdyT.stride(0), _ptr(xqT), xqT.stride(0), _ptr(sxT),
+        sxT.stride(0), M, N, K, _ptr(dw), dw.stride(0), 1 if accumulate else 0, None, 0, _stream(dyqT))
+    _lib.check(st, "fp8_block_gemm_wgrad")
+    return dw
+
+
+def fp8_e4m3_encode(x, q=None):
+    """Elementwise binary32 -> E4M3 codes with the library's device encoder."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 CUDA tensor")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    st = _lib.load().fp8_e4m3_encode(_ptr(x), _ptr(q), x.numel(), _stream(x))
+    _lib.check(st, "fp8_e4m3_encode")
+    return q
+
+
+def fp8_block_gemm_workspace_size(op, M, N, K):
+    return int(_lib.load().fp8_block_gemm_workspace_size(op, M, N, K))
+
+
+def fp8blk_version():
+    return _lib.load().fp8blk_version().decode()

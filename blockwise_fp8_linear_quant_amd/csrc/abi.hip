@@ -1,0 +1,186 @@
+// C ABI of libfp8blk: argument validation, device check, launches.
+// The semantics of each call are documented in include/fp8blk.h.
+#include <string.h>
+
+#include "fp8blk.h"
+#include "internal.h"
+
+namespace {
+
+using namespace fp8blk;
+
+// Per-device cache of "is gfx950" (0 = unknown, 1 = yes, 2 = no).  Benign race:
+// every writer stores the same value.
+constexpr int kMaxDevices = 64;
+int g_arch_ok[kMaxDevices];
+
+bool device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  if (dev < kMaxDevices && g_arch_ok[dev] != 0) return g_arch_ok[dev] == 1;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev] = ok ? 1 : 2;
+  return ok;
+}
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int finish() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP8BLK_OK : FP8BLK_LAUNCH_FAILED;
+}
+
+// Common checks for a GEMM operand pair; see fp8blk.h for the contract.
+int check_gemm(int64_t I, int64_t J, int64_t L, const void* A, int64_t lda, const float* SA, int64_t ldsa,
+               const void* B, int64_t ldb, const float* SB, int64_t ldsb, bool sb_rows,
+               const void* C, int64_t ldc, int out_mode, int64_t L_valid_rows_sa) {
+  if (I < 0 || J < 0 || L < 0) return FP8BLK_INVALID_ARG;
+  if (J % 128 != 0 || L % 128 != 0) return FP8BLK_UNSUPPORTED_SHAPE;
+  if (I == 0 || J == 0) return -1;  // valid no-op
+  if (C == nullptr) return FP8BLK_INVALID_ARG;
+  if (ldc < J) return FP8BLK_INVALID_ARG;
+  if (out_mode == OUT_BF16 ? (!al16(C) || ldc % 8 != 0) : (!al16(C) || ldc % 4 != 0)) return FP8BLK_MISALIGNED;
+  if (L == 0) return 0;
+  if (A == nullptr || B == nullptr || SA == nullptr || SB == nullptr) return FP8BLK_INVALID_ARG;
+  if (lda < L || ldb < L || ldsa < L_valid_rows_sa) return FP8BLK_INVALID_ARG;
+  if (sb_rows && ldsb < J) return FP8BLK_INVALID_ARG;
+  if (!al16(A) || !al16(B) || lda % 16 != 0 || ldb % 16 != 0) return FP8BLK_MISALIGNED;
+  if (!al16(SA) || ldsa % 4 != 0) return FP8BLK_MISALIGNED;
+  if (!al4(SB) || (sb_rows && (!al16(SB) || ldsb % 4 != 0))) return FP8BLK_MISALIGNED;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_1x128(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                    int transpose_out, uint8_t* q, int64_t ld_q,
+                    float* scales, int64_t ld_s, void* stream) {
+  if (rows < 0 || cols < 0 || (transpose_out != 0 && transpose_out != 1)) return FP8BLK_INVALID_ARG;
+  if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (x_bf16 == nullptr || q == nullptr || scales == nullptr) return FP8BLK_INVALID_ARG;
+  if (ld_x < cols) return FP8BLK_INVALID_ARG;
+  if (transpose_out == 0) {
+    if (ld_q < cols || ld_s < rows) return FP8BLK_INVALID_ARG;
+  } else {
+    const int64_t mpad = (rows + 127) / 128 * 128;
+    if (ld_q < mpad || ld_s < cols) return FP8BLK_INVALID_ARG;
+  }
+  if (!al16(x_bf16) || ld_x % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al4(scales)) return FP8BLK_MISALIGNED;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (transpose_out == 0)
+    launch_quant_rows(static_cast<const uint16_t*>(x_bf16), rows, cols, ld_x, q, ld_q, scales, ld_s, st);
+  else
+    launch_quant_tokens(static_cast<const uint16_t*>(x_bf16), rows, cols, ld_x, q, ld_q, scales, ld_s, st);
+  return finish();
+}
+
+int fp8_quant_128x128(const void* w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
+                      uint8_t* q, int64_t ld_q, float* scales,
+                      uint8_t* qT, int64_t ld_qT, float* scalesT, void* stream) {
+  if (rows < 0 || cols < 0) return FP8BLK_INVALID_ARG;
+  if ((qT == nullptr) != (scalesT == nullptr)) return FP8BLK_INVALID_ARG;
+  if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (w_bf16 == nullptr || q == nullptr || scales == nullptr) return FP8BLK_INVALID_ARG;
+  if (ld_w < cols || ld_q < cols || (qT != nullptr && ld_qT < rows)) return FP8BLK_INVALID_ARG;
+  if (!al16(w_bf16) || ld_w % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al4(scales)) return FP8BLK_MISALIGNED;
+  if (qT != nullptr && (!al16(qT) || ld_qT % 16 != 0 || !al4(scalesT))) return FP8BLK_MISALIGNED;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_quant_blocks(static_cast<const uint16_t*>(w_bf16), rows, cols, ld_w, q, ld_q, scales, qT, ld_qT,
+                      scalesT, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+int fp8_block_gemm_fwd(const uint8_t* xq, int64_t ld_xq, const float* sx, int64_t ld_sx,
+                       const uint8_t* wq, int64_t ld_wq, const float* sw,
+                       int64_t M, int64_t N, int64_t K,
+                       void* y, int64_t ld_y, int y_dtype,
+                       void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (y_dtype != FP8BLK_OUT_F32 && y_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
+  const int out = y_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
+  const int rc = check_gemm(M, N, K, xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, false, y, ld_y, out, M);
+  if (rc == -1) return FP8BLK_OK;
+  if (rc != 0) return rc;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_block_gemm(xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, SB_BLOCK, M, N, K, y, ld_y, out,
+                    static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+int fp8_block_gemm_dgrad(const uint8_t* dyq, int64_t ld_dyq, const float* sdy, int64_t ld_sdy,
+                         const uint8_t* wqT, int64_t ld_wqT, const float* swT,
+                         int64_t M, int64_t N, int64_t K,
+                         void* dx, int64_t ld_dx, int dx_dtype,
+                         void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (dx_dtype != FP8BLK_OUT_F32 && dx_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
+  const int out = dx_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
+  // C = dX [M, K]: rows I = M, columns J = K, contraction L = N.
+  const int rc = check_gemm(M, K, N, dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0, false, dx, ld_dx, out, M);
+  if (rc == -1) return FP8BLK_OK;
+  if (rc != 0) return rc;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_block_gemm(dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0, SB_BLOCK, M, K, N, dx, ld_dx, out,
+                    static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+int fp8_block_gemm_wgrad(const uint8_t* dyqT, int64_t ld_dyqT, const float* sdyT, int64_t ld_sdyT,
+                         const uint8_t* xqT, int64_t ld_xqT, const float* sxT, int64_t ld_sxT,
+                         int64_t M, int64_t N, int64_t K,
+                         float* dw, int64_t ld_dw, int accumulate,
+                         void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (accumulate != 0 && accumulate != 1) return FP8BLK_INVALID_ARG;
+  if (M < 0) return FP8BLK_INVALID_ARG;
+  const int64_t mpad = (M + 127) / 128 * 128;
+  const int out = accumulate ? OUT_F32_ACC : OUT_F32;
+  // C = dW [N, K]: rows I = N, columns J = K, contraction L = M_pad.
+  if (N % 128 != 0) return FP8BLK_UNSUPPORTED_SHAPE;
+  const int rc = check_gemm(N, K, mpad, dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT, ld_sxT, true, dw,
+                            ld_dw, out, N);
+  if (rc == -1) return FP8BLK_OK;
+  if (rc != 0) return rc;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_block_gemm(dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT, ld_sxT, SB_ROWS, N, K, mpad, dw, ld_dw, out,
+                    static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
+  (void)op; (void)M; (void)N; (void)K;
+  return 0;
+}
+
+int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, void* stream) {
+  if (n < 0) return FP8BLK_INVALID_ARG;
+  if (n == 0) return FP8BLK_OK;
+  if (x == nullptr || q == nullptr) return FP8BLK_INVALID_ARG;
+  if (!al4(x)) return FP8BLK_MISALIGNED;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_encode(x, q, n, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+const char* fp8blk_status_string(int status) {
+  switch (status) {
+    case FP8BLK_OK: return "ok";
+    case FP8BLK_INVALID_ARG: return "invalid argument";
+    case FP8BLK_UNSUPPORTED_SHAPE: return "unsupported shape (GEMM N and K must be multiples of 128)";
+    case FP8BLK_MISALIGNED: return "misaligned pointer or leading dimension";
+    case FP8BLK_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FP8BLK_DEVICE_UNSUPPORTED: return "device is not gfx950";
+    case FP8BLK_LAUNCH_FAILED: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* fp8blk_version(void) { return "fp8blk 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+// Launchers: arguments were validated by the ABI layer; these only enqueue.
+void launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                       uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+void launch_quant_tokens(const uint16_t* x, int64_t M, int64_t C, int64_t ldx,
+                         uint8_t* qT, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+void launch_quant_blocks(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
+                         uint8_t* q, int64_t ldq, float* s,
+                         uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
+void launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t st);
+
+// Scale modes of the second GEMM operand.
+enum SbMode { SB_BLOCK = 0, SB_ROWS = 1 };
+// Output modes.
+enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_F32_ACC = 2 };
+
+// C[I, J] = sum_lb SA(i, lb) SB(j, lb) sum_{l in lb} A[i, l] B[j, l]
+//   A [I, lda] codes, SA[lb * ldsa + i];
+//   B [J, ldb] codes; SB_BLOCK: SB[(j / 128) * nLB + lb]; SB_ROWS: SB[lb * ldsb + j].
+// J and L are multiples of 128; I is arbitrary.
+void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
+                       const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb, int sb_mode,
+                       int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode,
+                       hipStream_t st);
+
+}  // namespace fp8blk

@@ -1,0 +1,267 @@
+// Blockwise E4M3 quantisers for gfx950 (HBM-streaming kernels).
+//
+// Pages: arxiv-wiki summary of Puro-2B, section "접근 방법" item (4) -- FP8
+// E4M3 values with one scale per 1-D group of 128 activations and one per
+// 128x128 weight block; paperlayer.ai summary, appendix C "生産学習の詳細",
+// item "FP8実装pipeline" -- all three GEMMs of a linear layer (forward, data
+// gradient, weight gradient) take such operands.
+//
+// Every kernel reads BF16 once with 16-byte loads, reduces the group maximum
+// exactly (max of |x| in binary32), forms s = fl32(amax / 448) and writes
+// E4M3(fl32(x / s)) with the exact quotient of fp8_codec.h.  Zero groups get
+// s = 0 and codes 0x00.
+#include "internal.h"
+#include "fp8_codec.h"
+
+namespace fp8blk {
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(o));
+}
+// DPP controls (gfx9): quad_perm [1,0,3,2] = xor 1, quad_perm [2,3,0,1] = xor 2,
+// row_half_mirror reverses each 8-lane half, row_ror:8 = xor 8 inside a row of 16.
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kRor8 = 0x128;
+
+// Max over the 8 lanes {8a .. 8a+7}.
+__device__ __forceinline__ float max8(float v) {
+  v = dpp_fmax<kXor1>(v);
+  v = dpp_fmax<kXor2>(v);
+  return dpp_fmax<kHalfMirror>(v);
+}
+
+// Eight BF16 values starting at column col of a row; columns >= C read as +0.
+__device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ row, int64_t col, int64_t C) {
+  if (col + 8 <= C) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + col));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  uint32_t w[4] = {0, 0, 0, 0};
+  for (int i = 0; i < 8; ++i)
+    if (col + i < C) w[i >> 1] |= (uint32_t)row[col + i] << ((i & 1) * 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ float elem(const uint4& v, int i) {
+  const uint32_t w = (i >> 1) == 0 ? v.x : (i >> 1) == 1 ? v.y : (i >> 1) == 2 ? v.z : v.w;
+  return (i & 1) ? bits_f32(w & 0xffff0000u) : bits_f32(w << 16);
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, const GroupQ& g) {
+  return e4m3_encode(group_quotient(x, g)) & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return a | (b << 8) | (c << 16) | (d << 24);
+}
+
+// Store 8 code bytes at p[0..7], only columns col+i < C.
+__device__ __forceinline__ void store8(uint8_t* __restrict__ p, int64_t col, int64_t C, uint32_t lo, uint32_t hi) {
+  if (col + 8 <= C) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+    return;
+  }
+  for (int i = 0; i < 8; ++i)
+    if (col + i < C) p[i] = (uint8_t)(((i < 4) ? lo : hi) >> ((i & 3) * 8));
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise 1x128: a wave quantises 8 rows x one 128-column group; lane (r, c)
+// with r = lane/8, c = lane%8 holds columns [8c, 8c+8) and [64+8c, 64+8c+8)
+// so each load instruction covers 128 contiguous bytes per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
+  const int64_t g = blockIdx.y;
+  const int c = lane & 7;
+  const int64_t col0 = g * 128 + c * 8;
+  const int64_t col1 = col0 + 64;
+  const bool row_ok = row < R;
+
+  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+  if (row_ok) {
+    const uint16_t* p = x + row * ldx;
+    v0 = load8(p, col0, C);
+    v1 = load8(p, col1, C);
+  }
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[i] = elem(v0, i);
+    f[8 + i] = elem(v1, i);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = max8(amax);
+
+  const GroupQ gq = group_setup(amax);
+  const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;   // zero group -> codes 0x00
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    w[d] = keep & pack4(code_of(f[4 * d], gq), code_of(f[4 * d + 1], gq),
+                        code_of(f[4 * d + 2], gq), code_of(f[4 * d + 3], gq));
+  if (row_ok) {
+    uint8_t* qr = q + row * ldq;
+    if (col0 < C) store8(qr + col0, col0, C, w[0], w[1]);
+    if (col1 < C) store8(qr + col1, col1, C, w[2], w[3]);
+    if (c == 0) s[g * lds + row] = gq.s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token-dimension 1x128 with transposed output: a wave quantises 128 tokens x
+// 64 features.  Lane (b, c), b = lane/8, c = lane%8, loads tokens
+// [16b, 16b+16) x features [8c, 8c+8) (16-byte loads, 128 contiguous bytes
+// per token row per instruction) and writes, for each of its 8 features, the
+// 16 codes of its tokens as one 16-byte store -- the transpose happens in
+// registers.  The per-feature maximum over 128 tokens is a reduction over the
+// 8 lanes sharing c (lane distance 8, 16, 32).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_tokens_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t C, int64_t ldx,
+    uint8_t* __restrict__ qT, int64_t ldq, float* __restrict__ s, int64_t lds) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tg = blockIdx.y;
+  const int64_t f0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64 + (lane & 7) * 8;
+  const int b = lane >> 3;
+  const int64_t t0 = tg * 128 + b * 16;
+
+  uint4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t tok = t0 + i;
+    v[i] = (tok < M && f0 < C) ? load8(x + tok * ldx, f0, C) : make_uint4(0, 0, 0, 0);
+  }
+  float am[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(elem(v[i], j)));
+    m = dpp_fmax<kRor8>(m);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    am[j] = m;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const GroupQ gq = group_setup(am[j]);
+    const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      w[d] = keep & pack4(code_of(elem(v[4 * d], j), gq), code_of(elem(v[4 * d + 1], j), gq),
+                          code_of(elem(v[4 * d + 2], j), gq), code_of(elem(v[4 * d + 3], j), gq));
+    if (f0 + j < C) {
+      *reinterpret_cast<uint4*>(qT + (f0 + j) * ldq + t0) = make_uint4(w[0], w[1], w[2], w[3]);
+      if (b == 0) s[tg * lds + f0 + j] = gq.s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 blocks: a 256-thread workgroup quantises one block.  Thread (rb, c),
+// rb = t/16, c = t%16, holds rows [8rb, 8rb+8) x columns [8c, 8c+8); the block
+// maximum is reduced in the wave and across the 4 waves through LDS.  The
+// optional transposed copy is written from the same registers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_blocks_kernel(
+    const uint16_t* __restrict__ w, int64_t R, int64_t C, int64_t ldw,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT) {
+  __shared__ float red[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t br = blockIdx.y, bc = blockIdx.x;
+  const int c = t & 15, rb = t >> 4;
+  const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + i;
+    v[i] = (r < R && c0 < C) ? load8(w + r * ldw, c0, C) : make_uint4(0, 0, 0, 0);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(v[i], j)));
+  m = max8(m);
+  m = dpp_fmax<kRor8>(m);
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  const GroupQ gq = group_setup(m);
+  const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
+  uint32_t cd[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cd[i][j] = code_of(elem(v[i], j), gq);
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (r0 + i < R && c0 < C)
+      store8(q + (r0 + i) * ldq + c0, c0, C, keep & pack4(cd[i][0], cd[i][1], cd[i][2], cd[i][3]),
+             keep & pack4(cd[i][4], cd[i][5], cd[i][6], cd[i][7]));
+  }
+  if (qT != nullptr) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c0 + j < C && r0 < R)
+        store8(qT + (c0 + j) * ldqT + r0, r0, R, keep & pack4(cd[0][j], cd[1][j], cd[2][j], cd[3][j]),
+               keep & pack4(cd[4][j], cd[5][j], cd[6][j], cd[7][j]));
+    }
+  }
+  if (t == 0) {
+    const int64_t nbr = (R + 127) / 128, nbc = (C + 127) / 128;
+    s[br * nbc + bc] = gq.s;
+    if (sT != nullptr) sT[bc * nbr + br] = gq.s;
+  }
+}
+
+__global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x, uint8_t* __restrict__ q, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) q[i] = (uint8_t)e4m3_encode(x[i]);
+}
+
+}  // namespace
+
+void launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                       uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+  dim3 grid((unsigned)((R + 31) / 32), (unsigned)((C + 127) / 128));
+  hipLaunchKernelGGL(quant_rows_kernel, grid, dim3(256), 0, st, x, R, C, ldx, q, ldq, s, lds);
+}
+
+void launch_quant_tokens(const uint16_t* x, int64_t M, int64_t C, int64_t ldx,
+                         uint8_t* qT, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+  dim3 grid((unsigned)((C + 255) / 256), (unsigned)((M + 127) / 128));
+  hipLaunchKernelGGL(quant_tokens_kernel, grid, dim3(256), 0, st, x, M, C, ldx, qT, ldq, s, lds);
+}
+
+void launch_quant_blocks(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
+                         uint8_t* q, int64_t ldq, float* s,
+                         uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
+  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
+  hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, st, w, R, C, ldw, q, ldq, s, qT, ldqT, sT);
+}
+
+void launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t st) {
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(encode_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, q, n);
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,179 @@
+/*
+ * fp8blk -- blockwise-FP8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfp8blk.so.  The library implements the numerics that the
+ * Puro-2B report applies to its linear layers:
+ *   - arxiv-wiki summary "Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090
+ *     within $5090", section "접근 방법" (approach), item (4): the main linear
+ *     operations run in blockwise FP8 E4M3, with one scale per 1-D group of
+ *     128 activation values and one scale per 128x128 weight block; master
+ *     weights and optimizer state stay BF16/FP32;
+ *   - paperlayer.ai summary of arXiv 2608.27370v1, appendix C
+ *     "生産学習の詳細", item "FP8実装pipeline": the FP8 GEMMs are the
+ *     forward, data-gradient and weight-gradient products of each linear
+ *     layer; gradients stay FP32, the hidden/residual flow stays BF16.
+ *
+ * Numerics (readings where the pages are silent; the CPU oracle follows the
+ * same readings):
+ *   - E4M3 is the OCP encoding (largest finite 448, subnormals kept, 0x7F NaN);
+ *   - a group's scale is the binary32 dequantisation multiplier
+ *     s = fl32(amax / 448), amax = max |x| over the group's valid elements;
+ *   - code = E4M3_RNE_saturating(fl32(x / s)); an all-zero group has s = 0 and
+ *     codes 0x00; binary32 denormals are not flushed;
+ *   - GEMMs accumulate each 128-wide block product exactly in FP8 MFMA (FP32
+ *     partial), multiply it by the product of the two block scales in FP32 and
+ *     add it to an FP32 accumulator; BF16 outputs are rounded to nearest even.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees, synchronises or keeps state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting.  Device faults surface at the caller's
+ *     next synchronisation.
+ *   - Matrices are row-major with an explicit leading dimension `ld_*` in
+ *     elements (BF16: 2 bytes, codes: 1 byte, FP32: 4 bytes).
+ *   - Arguments are validated before anything is launched; on error nothing is
+ *     written and a non-zero fp8blk_status is returned.  Problems with a zero
+ *     dimension are valid no-ops.
+ *   - Code and BF16 matrices must start on 16-byte boundaries and have leading
+ *     dimensions that are multiples of 16 bytes; scale arrays need 4-byte
+ *     alignment; FP32 outputs 16-byte alignment with ld a multiple of 4.
+ *   - Calls on one stream are ordered; calls on different streams that write
+ *     the same buffers race.
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8blk_status {
+  FP8BLK_OK = 0,
+  FP8BLK_INVALID_ARG = 1,        /* null pointer, negative size, ld too small, bad enum */
+  FP8BLK_UNSUPPORTED_SHAPE = 2,  /* GEMM: N or K not a multiple of 128 */
+  FP8BLK_MISALIGNED = 3,         /* pointer or leading dimension alignment */
+  FP8BLK_WORKSPACE_TOO_SMALL = 4,
+  FP8BLK_DEVICE_UNSUPPORTED = 5, /* current device is not gfx950 */
+  FP8BLK_LAUNCH_FAILED = 6       /* hipGetLastError() after a launch */
+} fp8blk_status;
+
+enum { FP8BLK_OUT_F32 = 0, FP8BLK_OUT_BF16 = 1 };
+enum { FP8BLK_OP_FWD = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2 };
+
+/*
+ * 1x128 group quantiser of a BF16 matrix x [rows, cols] (ld_x >= cols).
+ * Source: arxiv-wiki Puro-2B summary, section "접근 방법" item (4) (1-D
+ * activation groups of 128, E4M3 values).
+ *
+ * transpose_out = 0 (row-wise; the fwd operand X and the dgrad operand dY):
+ *   groups are 128 consecutive columns of a row (the last group of a row may be
+ *   shorter); q [rows, ld_q >= cols] holds the codes in x's layout;
+ *   scales are group-major: scales[g * ld_s + r] for group g of row r,
+ *   ld_s >= rows, g < ceil(cols/128).
+ * transpose_out = 1 (token-dimension; the wgrad operands X^T and dY^T):
+ *   rows are tokens; groups are 128 consecutive rows (tokens) of a column;
+ *   q [cols, ld_q >= round_up(rows, 128)] holds the codes transposed (tokens
+ *   contiguous), with the padding tokens rows..round_up(rows,128)-1 written as
+ *   0x00; scales[g * ld_s + c] for token group g of column c, ld_s >= cols,
+ *   g < ceil(rows/128).
+ */
+int fp8_quant_1x128(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                    int transpose_out, uint8_t* q, int64_t ld_q,
+                    float* scales, int64_t ld_s, void* stream);
+
+/*
+ * 128x128 block quantiser of a BF16 weight w [rows, cols] (ld_w >= cols).
+ * Source: arxiv-wiki Puro-2B summary, section "접근 방법" item (4) (one scale
+ * per 128x128 weight block); the transposed copy serves the data-gradient GEMM
+ * (paperlayer.ai summary, appendix C, item "FP8実装pipeline").
+ *
+ * q [rows, ld_q >= cols]; scales dense row-major [ceil(rows/128), ceil(cols/128)].
+ * If qT is non-NULL, also writes Q(w^T): qT [cols, ld_qT >= rows] with
+ * qT[c * ld_qT + r] = q[r * ld_q + c], and scalesT dense row-major
+ * [ceil(cols/128), ceil(rows/128)] (the transpose of scales).  qT and scalesT
+ * are both NULL or both non-NULL.  Edge blocks use only their valid elements.
+ */
+int fp8_quant_128x128(const void* w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
+                      uint8_t* q, int64_t ld_q, float* scales,
+                      uint8_t* qT, int64_t ld_qT, float* scalesT, void* stream);
+
+/*
+ * Forward GEMM  Y[M, N] = sum_kb Sx[m, kb] * Sw[n/128, kb] * sum_{k in kb} X[m, k] W[n, k].
+ * Source: paperlayer.ai Puro-2B summary, appendix C, item "FP8実装pipeline"
+ * (forward GEMM in blockwise E4M3).
+ *
+ * xq [M, ld_xq >= K] codes with row-wise scales sx[kb * ld_sx + m] (the
+ *   transpose_out = 0 layout of fp8_quant_1x128, ld_sx >= M);
+ * wq [N, ld_wq >= K] codes with block scales sw dense [N/128, K/128];
+ * y  [M, ld_y >= N], FP32 or BF16 (y_dtype).
+ * N and K must be multiples of 128; M is arbitrary.  ws/ws_bytes: workspace
+ * (may be NULL/0 when fp8_block_gemm_workspace_size returns 0).
+ */
+int fp8_block_gemm_fwd(const uint8_t* xq, int64_t ld_xq, const float* sx, int64_t ld_sx,
+                       const uint8_t* wq, int64_t ld_wq, const float* sw,
+                       int64_t M, int64_t N, int64_t K,
+                       void* y, int64_t ld_y, int y_dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Data-gradient GEMM  dX[M, K] = dY[M, N] . W[N, K], contraction over N.
+ * Source: paperlayer.ai Puro-2B summary, appendix C, item "FP8実装pipeline"
+ * (data-gradient GEMM in blockwise E4M3).
+ *
+ * dyq [M, ld_dyq >= N] codes with row-wise scales sdy[nb * ld_sdy + m];
+ * wqT [K, ld_wqT >= N] = Q(W^T) codes with block scales swT dense [K/128, N/128]
+ *   (the qT/scalesT outputs of fp8_quant_128x128 on W);
+ * dx [M, ld_dx >= K], FP32 or BF16.
+ * N and K must be multiples of 128; M is arbitrary.
+ */
+int fp8_block_gemm_dgrad(const uint8_t* dyq, int64_t ld_dyq, const float* sdy, int64_t ld_sdy,
+                         const uint8_t* wqT, int64_t ld_wqT, const float* swT,
+                         int64_t M, int64_t N, int64_t K,
+                         void* dx, int64_t ld_dx, int dx_dtype,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weight-gradient GEMM  dW[N, K] (+)= dY^T[N, M] . X[M, K], contraction over
+ * the M tokens in groups of 128 (padded to round_up(M, 128) with zero codes).
+ * Source: paperlayer.ai Puro-2B summary, appendix C, item "FP8実装pipeline"
+ * (weight-gradient GEMM in blockwise E4M3, gradients in FP32).
+ *
+ * dyqT [N, ld_dyqT >= round_up(M,128)] token-dimension codes of dY with scales
+ *   sdyT[mb * ld_sdyT + n]; xqT [K, ld_xqT >= round_up(M,128)] token-dimension
+ *   codes of X with scales sxT[mb * ld_sxT + k] (fp8_quant_1x128 with
+ *   transpose_out = 1);
+ * dw [N, ld_dw >= K] FP32; accumulate = 0 overwrites, 1 adds to dw.
+ * N and K must be multiples of 128; M is arbitrary.
+ */
+int fp8_block_gemm_wgrad(const uint8_t* dyqT, int64_t ld_dyqT, const float* sdyT, int64_t ld_sdyT,
+                         const uint8_t* xqT, int64_t ld_xqT, const float* sxT, int64_t ld_sxT,
+                         int64_t M, int64_t N, int64_t K,
+                         float* dw, int64_t ld_dw, int accumulate,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes a GEMM call needs for (op, M, N, K); 0 means none. */
+size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K);
+
+/*
+ * The library's binary32 -> E4M3 encoder applied elementwise: q[i] = E4M3(x[i])
+ * with round-to-nearest-even, saturation at +-448 and the sign kept (OCP E4M3,
+ * the format named in the arxiv-wiki Puro-2B summary, "접근 방법" item (4)).
+ * Exposed so the device encoder can be checked on every binary32 input.
+ * x: n floats, q: n bytes, both device pointers (no alignment requirement).
+ */
+int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* fp8blk_status_string(int status);
+
+/* Library version string (static). */
+const char* fp8blk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8BLK_H */

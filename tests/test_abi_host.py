@@ -1,0 +1,100 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+
+
+def _lib():
+    from blockwise_fp8_linear_quant_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libfp8blk.so is not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n.startswith("fp8")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_block_gemm_fwd", "fp8_block_gemm_dgrad",
+              "fp8_block_gemm_wgrad", "fp8_block_gemm_workspace_size", "fp8blk_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    from blockwise_fp8_linear_quant_amd import _lib as L
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, f"binding lacks a signature for {n}"
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.fp8blk_status_string(0) == b"ok"
+    assert b"128" in lib.fp8blk_status_string(2)
+    assert lib.fp8blk_status_string(99) == b"unknown status"
+    assert b"gfx950" in lib.fp8blk_version()
+    assert lib.fp8_block_gemm_workspace_size(0, 4096, 4096, 2048) == 0
+
+
+def test_validation_happens_before_launch():
+    lib = _lib()
+    P = ctypes.c_void_p(16)       # aligned dummy address, never dereferenced on the error paths
+    Q = ctypes.c_void_p(17)       # misaligned
+    # negative sizes / bad enum
+    assert lib.fp8_quant_1x128(P, -1, 128, 128, 0, P, 128, P, 16, None) == 1
+    assert lib.fp8_quant_1x128(P, 16, 128, 128, 2, P, 128, P, 16, None) == 1
+    # ld too small
+    assert lib.fp8_quant_1x128(P, 16, 128, 64, 0, P, 128, P, 16, None) == 1
+    assert lib.fp8_quant_1x128(P, 300, 128, 128, 1, P, 256, P, 128, None) == 1   # ld_q < round_up(300,128)
+    # null pointers
+    assert lib.fp8_quant_1x128(None, 16, 128, 128, 0, P, 128, P, 16, None) == 1
+    # misalignment
+    assert lib.fp8_quant_1x128(Q, 16, 128, 128, 0, P, 128, P, 16, None) == 3
+    assert lib.fp8_quant_1x128(P, 16, 128, 132, 0, P, 128, P, 16, None) == 3
+    # zero-size problems are valid no-ops, even with null pointers
+    assert lib.fp8_quant_1x128(None, 0, 128, 128, 0, None, 128, None, 16, None) == 0
+    assert lib.fp8_quant_128x128(None, 5, 0, 0, None, 0, None, None, 0, None, None) == 0
+    # qT / scalesT must come together
+    assert lib.fp8_quant_128x128(P, 128, 128, 128, P, 128, P, P, 128, None, None) == 1
+    # GEMM shapes: N, K multiples of 128
+    assert lib.fp8_block_gemm_fwd(P, 256, P, 16, P, 256, P, 16, 200, 256, P, 200, 0, None, 0, None) == 2
+    assert lib.fp8_block_gemm_fwd(P, 256, P, 16, P, 256, P, 16, 256, 200, P, 256, 0, None, 0, None) == 2
+    assert lib.fp8_block_gemm_dgrad(P, 256, P, 16, P, 256, P, 16, 100, 256, P, 100, 1, None, 0, None) == 2
+    assert lib.fp8_block_gemm_wgrad(P, 128, P, 16, P, 128, P, 128, 100, 130, 128, P, 128, 0, None, 0, None) == 2
+    # bad dtype / accumulate flags
+    assert lib.fp8_block_gemm_fwd(P, 256, P, 16, P, 256, P, 16, 256, 256, P, 256, 7, None, 0, None) == 1
+    assert lib.fp8_block_gemm_wgrad(P, 128, P, 128, P, 128, P, 128, 100, 128, 128, P, 128, 2, None, 0, None) == 1
+    # GEMM ld checks
+    assert lib.fp8_block_gemm_fwd(P, 128, P, 16, P, 256, P, 16, 256, 256, P, 256, 0, None, 0, None) == 1
+    assert lib.fp8_block_gemm_fwd(P, 256, P, 8, P, 256, P, 16, 256, 256, P, 256, 0, None, 0, None) == 1
+    # GEMM misalignment (ld_sx not a multiple of 4, odd pointer)
+    assert lib.fp8_block_gemm_fwd(P, 256, P, 18, P, 256, P, 16, 256, 256, P, 256, 0, None, 0, None) == 3
+    assert lib.fp8_block_gemm_fwd(Q, 256, P, 16, P, 256, P, 16, 256, 256, P, 256, 0, None, 0, None) == 3
+    # zero-size GEMMs are no-ops
+    assert lib.fp8_block_gemm_fwd(None, 0, None, 0, None, 0, None, 0, 0, 256, None, 0, 0, None, 0, None) == 0
+    assert lib.fp8_e4m3_encode(None, None, 0, None) == 0
+    assert lib.fp8_e4m3_encode(P, P, -1, None) == 1
+
+
+def test_binding_raises_without_library(tmp_path):
+    from blockwise_fp8_linear_quant_amd import _lib as L
+    saved = L._lib
+    try:
+        L._lib = None
+        with pytest.raises(ImportError):
+            L.load(str(tmp_path / "missing.so"))
+    finally:
+        L._lib = saved
