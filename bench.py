@@ -1,0 +1,206 @@
+"""Benchmark of the blockwise-FP8 linear layer hot path on one MI355X.
+
+One step = one decoder layer's linear work at M tokens (default 4096, hidden
+2048, intermediate 6144), everything the path computes:
+  for each linear (qkv, o, gate_up, down):
+    quantise X (1x128 row-wise and token-dimension), W (128x128 with the
+    transposed copy) and dY (row-wise and token-dimension), then
+    forward Y = X W^T (BF16 out), dgrad dX = dY W (BF16 out),
+    wgrad dW = dY^T X (FP32 out).
+Inputs are seeded synthetic BF16 tensors (X ~ N(0,1), W ~ N(0,0.02),
+dY ~ N(0,1e-3)) already resident in HBM; outputs are preallocated, so the
+timed region holds only kernel launches of libfp8blk.
+
+Prints one JSON line.  `value` is GEMM TFLOP/s of the whole step (the 12 GEMMs'
+2*M*N*K divided by the step time, quantisers included).  `roofline` covers
+the dominant kernel (the block GEMM), timed with HIP events on the stream the
+kernels run on.  `cpu_baseline` times the numpy oracle on a bounded token
+sample of the same layer.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    return ap.parse_args()
+
+
+class LayerBuffers:
+    """Device inputs and preallocated outputs for one linear of the layer."""
+
+    def __init__(self, torch, B, W, name, k, n, M, dev):
+        import numpy as np
+        self.name, self.k, self.n, self.M = name, k, n, M
+        cfg = 2
+        self.xb = W.normal_bf16((M, k), 1.0, W.seed_for(cfg, 0, name, "x"))
+        self.wb = W.normal_bf16((n, k), 0.02, W.seed_for(cfg, 0, name, "w"))
+        self.dyb = W.normal_bf16((M, n), 1e-3, W.seed_for(cfg, 0, name, "dy"))
+        to = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.x, self.w, self.dy = to(self.xb), to(self.wb), to(self.dyb)
+        # Outputs (allocated once, reused every step).
+        self.xq, self.sx = B.fp8_quant_1x128(self.x)
+        self.xqT, self.sxT = B.fp8_quant_1x128(self.x, transpose_out=True)
+        self.wq, self.sw, self.wqT, self.swT = B.fp8_quant_128x128(self.w, with_transpose=True)
+        self.dyq, self.sdy = B.fp8_quant_1x128(self.dy)
+        self.dyqT, self.sdyT = B.fp8_quant_1x128(self.dy, transpose_out=True)
+        self.y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        self.dx = torch.empty((M, k), dtype=torch.bfloat16, device=dev)
+        self.dw = torch.empty((n, k), dtype=torch.float32, device=dev)
+
+    def flops(self):
+        return 3 * 2 * self.M * self.n * self.k
+
+    def quant_bytes(self):
+        M, n, k = self.M, self.n, self.k
+        row = lambda r, c: r * c * 3 + r * (-(-c // 128)) * 4          # 2 B in, 1 B out, scales
+        tok = lambda r, c: r * c * 2 + c * (-(-r // 128) * 128) + c * (-(-r // 128)) * 4
+        blk = n * k * 2 + 2 * n * k + 2 * 4 * (-(-n // 128)) * (-(-k // 128))
+        return row(M, k) + tok(M, k) + blk + row(M, n) + tok(M, n)
+
+    def quantise(self, B):
+        B.fp8_quant_1x128(self.x, q=self.xq, scales=self.sx)
+        B.fp8_quant_1x128(self.x, transpose_out=True, q=self.xqT, scales=self.sxT)
+        B.fp8_quant_128x128(self.w, True, self.wq, self.sw, self.wqT, self.swT)
+        B.fp8_quant_1x128(self.dy, q=self.dyq, scales=self.sdy)
+        B.fp8_quant_1x128(self.dy, transpose_out=True, q=self.dyqT, scales=self.sdyT)
+
+    def gemms(self, B):
+        B.fp8_block_gemm_fwd(self.xq, self.sx, self.wq, self.sw, y=self.y)
+        B.fp8_block_gemm_dgrad(self.dyq, self.sdy, self.wqT, self.swT, dx=self.dx)
+        B.fp8_block_gemm_wgrad(self.dyqT, self.sdyT, self.xqT, self.sxT, M=self.M, dw=self.dw)
+
+
+def cpu_baseline(W, layers, sample_tokens):
+    """The numpy oracle on the first `sample_tokens` tokens of every linear of the layer."""
+    import numpy as np
+    from oracle import gemm, quant
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    flops = 0
+    t0 = time.perf_counter()
+    for L in layers:
+        xs, dys = L.xb[:sample_tokens], L.dyb[:sample_tokens]
+        xq, sx = quant.quant_1x128_rows(xs)
+        xqT, sxT = quant.quant_1x128_tokens(xs)
+        wq, sw = quant.quant_128x128(L.wb)
+        wqT, swT = quant.quant_128x128(np.ascontiguousarray(L.wb.T))
+        dyq, sdy = quant.quant_1x128_rows(dys)
+        dyqT, sdyT = quant.quant_1x128_tokens(dys)
+        gemm.fwd(xq, sx, wq, sw, budget=False)
+        gemm.dgrad(dyq, sdy, wqT, swT, budget=False)
+        gemm.wgrad(dyqT, sdyT, xqT, sxT, budget=False)
+        flops += 3 * 2 * sample_tokens * L.n * L.k
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one layer's 4 linears (quantisers + fwd/dgrad/wgrad) on the first {sample_tokens} "
+                      f"tokens, numpy float64 oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from blockwise_fp8_linear_quant_amd import binding as B
+    from blockwise_fp8_linear_quant_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    M = args.tokens
+    layers = [LayerBuffers(torch, B, W, n, k, nout, M, dev) for n, k, nout in W.LINEARS]
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        for i, L in enumerate(layers):
+            if evs is not None:
+                evs[i][0].record()
+            L.quantise(B)
+            if evs is not None:
+                evs[i][1].record()
+            L.gemms(B)
+            if evs is not None:
+                evs[i][2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, GEMM launches bracketed by events on the current stream.
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[(mk(), mk(), mk()) for _ in layers] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+
+    gemm_ms = sum(b.elapsed_time(c) for row in evs for (a, b, c) in row) / args.steps
+    quant_ms = sum(a.elapsed_time(b) for row in evs for (a, b, c) in row) / args.steps
+    flops = sum(L.flops() for L in layers)
+    value = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["f16"]
+    qbytes = sum(L.quant_bytes() for L in layers)
+
+    out = {
+        "metric": "Blockwise-FP8 GEMM TFLOP/s + % FP8 MFMA peak, 2B-layer shapes, M=4096",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"one Puro-2B decoder layer's linears (qkv 2048->4096, o 2048->2048, "
+                               f"gate_up 2048->12288, down 6144->2048), quantise + fwd + dgrad + wgrad",
+                   "tokens": M, "hidden": 2048, "intermediate": 6144, "gemm_gflop_per_step": round(flops / 1e9, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / peak, 4), "traffic": None,
+                     "kernel": "block_gemm_kernel (E4M3 codes -> exact F16 MFMA, FP32 block rescale)",
+                     "gemm_ms_per_step": round(gemm_ms, 4),
+                     "frac_of_fp8_peak": round(gemm_tflops / PEAK_TFLOPS["fp8"], 4)},
+        "quantisers": {"ms_per_step": round(quant_ms, 4), "algorithmic_gb": round(qbytes / 1e9, 4),
+                       "gbps": round(qbytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms > 0 else None,
+                       "frac_hbm_peak": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                       if quant_ms > 0 else None},
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, layers, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

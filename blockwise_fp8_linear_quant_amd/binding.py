@@ -44,6 +44,12 @@ def _check_2d(t, dtype, name):
         raise ValueError(f"{name} must have unit column stride")
 
 
+def _codes(rows, cols, device):
+    """uint8 [rows, cols] view of a buffer whose leading dimension is a multiple of 16 bytes."""
+    ld = _round_up(max(cols, 1), 16)
+    return torch.empty((rows, ld), dtype=torch.uint8, device=device)[:, :cols]
+
+
 def _scales(rows, cols, device):
     """float32 [rows, cols] view of a buffer whose leading dimension is a multiple of 4."""
     ld = _round_up(max(cols, 1), 4)
@@ -56,7 +62,7 @@ def fp8_quant_1x128(x, transpose_out=False, q=None, scales=None):
     R, C = x.shape
     if not transpose_out:
         if q is None:
-            q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+            q = _codes(R, C, x.device)
         if scales is None:
             scales = _scales(-(-C // 128), R, x.device)
     else:
@@ -77,12 +83,12 @@ def fp8_quant_128x128(w, with_transpose=False, q=None, scales=None, qT=None, sca
     R, C = w.shape
     br, bc = -(-R // 128), -(-C // 128)
     if q is None:
-        q = torch.empty((R, C), dtype=torch.uint8, device=w.device)
+        q = _codes(R, C, w.device)
     if scales is None:
         scales = torch.empty((br, bc), dtype=torch.float32, device=w.device)
     if with_transpose:
         if qT is None:
-            qT = torch.empty((C, R), dtype=torch.uint8, device=w.device)
+            qT = _codes(C, R, w.device)
         if scalesT is None:
             scalesT = torch.empty((bc, br), dtype=torch.float32, device=w.device)
     st = _lib.load().fp8_quant_128x128(

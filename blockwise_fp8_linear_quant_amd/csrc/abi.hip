@@ -108,7 +108,7 @@ int fp8_block_gemm_fwd(const uint8_t* xq, int64_t ld_xq, const float* sx, int64_
   if (rc == -1) return FP8BLK_OK;
   if (rc != 0) return rc;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  launch_block_gemm(xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, SB_BLOCK, M, N, K, y, ld_y, out,
+  launch_block_gemm(xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, SB_BLOCK, M, N, K, y, ld_y, out, 0,
                     static_cast<hipStream_t>(stream));
   return finish();
 }
@@ -126,7 +126,7 @@ int fp8_block_gemm_dgrad(const uint8_t* dyq, int64_t ld_dyq, const float* sdy, i
   if (rc == -1) return FP8BLK_OK;
   if (rc != 0) return rc;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  launch_block_gemm(dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0, SB_BLOCK, M, K, N, dx, ld_dx, out,
+  launch_block_gemm(dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0, SB_BLOCK, M, K, N, dx, ld_dx, out, 0,
                     static_cast<hipStream_t>(stream));
   return finish();
 }
@@ -148,7 +148,7 @@ int fp8_block_gemm_wgrad(const uint8_t* dyqT, int64_t ld_dyqT, const float* sdyT
   if (rc == -1) return FP8BLK_OK;
   if (rc != 0) return rc;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  launch_block_gemm(dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT, ld_sxT, SB_ROWS, N, K, mpad, dw, ld_dw, out,
+  launch_block_gemm(dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT, ld_sxT, SB_ROWS, N, K, mpad, dw, ld_dw, out, 0,
                     static_cast<hipStream_t>(stream));
   return finish();
 }

@@ -27,6 +27,6 @@ enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_F32_ACC = 2 };
 void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                        const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb, int sb_mode,
                        int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode,
-                       hipStream_t st);
+                       int prec, hipStream_t st);
 
 }  // namespace fp8blk

@@ -11,8 +11,14 @@ def say(*a):
 
 
 def dev_bf16(bits, device="cuda:0"):
+    """BF16 device tensor [R, C]; the row stride is padded to a multiple of 8 elements (16 bytes)."""
     import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+    R, C = bits.shape
+    ld = -(-max(C, 1) // 8) * 8
+    buf = np.zeros((R, ld), dtype=np.uint16)
+    buf[:, :C] = bits
+    t = torch.from_numpy(buf.view(np.int16)).to(device).view(torch.bfloat16)
+    return t[:, :C]
 
 
 def host(t):
