@@ -112,11 +112,29 @@ def _dtype_code(t):
     raise TypeError("output must be float32 or bfloat16")
 
 
-def fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None):
+FLAG_EXACT_BLOCKS = 0
+FLAG_FP8_MATRIX_CORE = 1
+OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
+
+
+def fp8_block_gemm(op, a, sa, b, sb, M, N, K, c, accumulate=False, fp8_matrix_core=False):
+    """The generic C entry point (explicit op and matrix path); c is preallocated."""
+    ld_sb = sb.stride(0) if op == OP_WGRAD else 0
+    st = _lib.load().fp8_block_gemm(
+        op, FLAG_FP8_MATRIX_CORE if fp8_matrix_core else FLAG_EXACT_BLOCKS,
+        _ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b), b.stride(0), _ptr(sb), ld_sb,
+        M, N, K, _ptr(c), c.stride(0), _dtype_code(c), 1 if accumulate else 0, None, 0, _stream(a))
+    _lib.check(st, "fp8_block_gemm")
+    return c
+
+
+def fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None, fp8_matrix_core=False):
     """Y[M, N] = Xq . Wq^T with 1x128 row scales sx [K/128, M] and block scales sw [N/128, K/128]."""
     M, K = xq.shape
     N = wq.shape[0]
     y = _out((M, N), out_dtype, xq.device, y)
+    if fp8_matrix_core:
+        return fp8_block_gemm(OP_FWD, xq, sx, wq, sw, M, N, K, y, fp8_matrix_core=True)
     st = _lib.load().fp8_block_gemm_fwd(
         _ptr(xq), xq.stride(0), _ptr(sx), sx.stride(0), _ptr(wq), wq.stride(0), _ptr(sw),
         M, N, K, _ptr(y), y.stride(0), _dtype_code(y), None, 0, _stream(xq))
@@ -124,11 +142,13 @@ def fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None):
     return y
 
 
-def fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, dx=None):
+def fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, dx=None, fp8_matrix_core=False):
     """dX[M, K] = dY . W from dYq [M, N] (row scales sdy [N/128, M]) and WqT [K, N] (scales swT [K/128, N/128])."""
     M, N = dyq.shape
     K = wqT.shape[0]
     dx = _out((M, K), out_dtype, dyq.device, dx)
+    if fp8_matrix_core:
+        return fp8_block_gemm(OP_DGRAD, dyq, sdy, wqT, swT, M, N, K, dx, fp8_matrix_core=True)
     st = _lib.load().fp8_block_gemm_dgrad(
         _ptr(dyq), dyq.stride(0), _ptr(sdy), sdy.stride(0), _ptr(wqT), wqT.stride(0), _ptr(swT),
         M, N, K, _ptr(dx), dx.stride(0), _dtype_code(dx), None, 0, _stream(dyq))
@@ -136,7 +156,7 @@ def fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, dx=None):
     return dx
 
 
-def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False):
+def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False, fp8_matrix_core=False):
     """dW[N, K] (+)= dY^T . X from token-dimension codes dyqT [N, M_pad], xqT [K, M_pad]."""
     N = dyqT.shape[0]
     K = xqT.shape[0]
@@ -146,6 +166,8 @@ def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False
         if accumulate:
             raise ValueError("accumulate=True needs an existing dw")
         dw = torch.empty((N, K), dtype=torch.float32, device=dyqT.device)
+    if fp8_matrix_core:
+        return fp8_block_gemm(OP_WGRAD, dyqT, sdyT, xqT, sxT, M, N, K, dw, accumulate, fp8_matrix_core=True)
     st = _lib.load().fp8_block_gemm_wgrad(
         _ptr(dyqT), dyqT.stride(0), _ptr(sdyT), sdyT.stride(0), _ptr(xqT), xqT.stride(0), _ptr(sxT),
         sxT.stride(0), M, N, K, _ptr(dw), dw.stride(0), 1 if accumulate else 0, None, 0, _stream(dyqT))

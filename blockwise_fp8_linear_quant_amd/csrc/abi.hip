@@ -96,21 +96,60 @@ int fp8_quant_128x128(const void* w_bf16, int64_t rows, int64_t cols, int64_t ld
   return finish();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared body of the GEMM entry points.  Operand naming follows the generic
+// entry point: a/sa is the row-scaled operand, b/sb the second one.
+int gemm_impl(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+              const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
+              int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, int accumulate,
+              hipStream_t st) {
+  if (op != FP8BLK_OP_FWD && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return FP8BLK_INVALID_ARG;
+  if (flags != FP8BLK_GEMM_EXACT_BLOCKS && flags != FP8BLK_GEMM_FP8_MATRIX_CORE) return FP8BLK_INVALID_ARG;
+  if (c_dtype != FP8BLK_OUT_F32 && c_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
+  if (accumulate != 0 && accumulate != 1) return FP8BLK_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return FP8BLK_INVALID_ARG;
+  const int prec = flags == FP8BLK_GEMM_FP8_MATRIX_CORE ? 1 : 0;
+  int64_t I, J, L;
+  int sb_mode, out;
+  if (op == FP8BLK_OP_WGRAD) {
+    // C = dW [N, K]: rows I = N, columns J = K, contraction over M_pad tokens.
+    if (c_dtype != FP8BLK_OUT_F32) return FP8BLK_INVALID_ARG;
+    if (N % 128 != 0) return FP8BLK_UNSUPPORTED_SHAPE;
+    I = N; J = K; L = (M + 127) / 128 * 128;
+    sb_mode = SB_ROWS;
+    out = accumulate ? OUT_F32_ACC : OUT_F32;
+  } else {
+    if (accumulate) return FP8BLK_INVALID_ARG;
+    // fwd: C = Y [M, N] over K;  dgrad: C = dX [M, K] over N.
+    I = M;
+    J = op == FP8BLK_OP_FWD ? N : K;
+    L = op == FP8BLK_OP_FWD ? K : N;
+    sb_mode = SB_BLOCK;
+    out = c_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
+  }
+  const int rc = check_gemm(I, J, L, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, sb_mode == SB_ROWS, c, ld_c, out, I);
+  if (rc == -1) return FP8BLK_OK;
+  if (rc != 0) return rc;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_block_gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, sb_mode, I, J, L, c, ld_c, out, prec, st);
+  return finish();
+}
+
+}  // namespace
+
+extern "C" {
+
 int fp8_block_gemm_fwd(const uint8_t* xq, int64_t ld_xq, const float* sx, int64_t ld_sx,
                        const uint8_t* wq, int64_t ld_wq, const float* sw,
                        int64_t M, int64_t N, int64_t K,
                        void* y, int64_t ld_y, int y_dtype,
                        void* ws, size_t ws_bytes, void* stream) {
   (void)ws; (void)ws_bytes;
-  if (y_dtype != FP8BLK_OUT_F32 && y_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
-  const int out = y_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
-  const int rc = check_gemm(M, N, K, xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, false, y, ld_y, out, M);
-  if (rc == -1) return FP8BLK_OK;
-  if (rc != 0) return rc;
-  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  launch_block_gemm(xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, SB_BLOCK, M, N, K, y, ld_y, out, 0,
-                    static_cast<hipStream_t>(stream));
-  return finish();
+  return gemm_impl(FP8BLK_OP_FWD, FP8BLK_GEMM_EXACT_BLOCKS, xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, M, N, K,
+                   y, ld_y, y_dtype, 0, static_cast<hipStream_t>(stream));
 }
 
 int fp8_block_gemm_dgrad(const uint8_t* dyq, int64_t ld_dyq, const float* sdy, int64_t ld_sdy,
@@ -119,16 +158,8 @@ int fp8_block_gemm_dgrad(const uint8_t* dyq, int64_t ld_dyq, const float* sdy, i
                          void* dx, int64_t ld_dx, int dx_dtype,
                          void* ws, size_t ws_bytes, void* stream) {
   (void)ws; (void)ws_bytes;
-  if (dx_dtype != FP8BLK_OUT_F32 && dx_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
-  const int out = dx_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
-  // C = dX [M, K]: rows I = M, columns J = K, contraction L = N.
-  const int rc = check_gemm(M, K, N, dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0, false, dx, ld_dx, out, M);
-  if (rc == -1) return FP8BLK_OK;
-  if (rc != 0) return rc;
-  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  launch_block_gemm(dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0, SB_BLOCK, M, K, N, dx, ld_dx, out, 0,
-                    static_cast<hipStream_t>(stream));
-  return finish();
+  return gemm_impl(FP8BLK_OP_DGRAD, FP8BLK_GEMM_EXACT_BLOCKS, dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0,
+                   M, N, K, dx, ld_dx, dx_dtype, 0, static_cast<hipStream_t>(stream));
 }
 
 int fp8_block_gemm_wgrad(const uint8_t* dyqT, int64_t ld_dyqT, const float* sdyT, int64_t ld_sdyT,
@@ -137,20 +168,17 @@ int fp8_block_gemm_wgrad(const uint8_t* dyqT, int64_t ld_dyqT, const float* sdyT
                          float* dw, int64_t ld_dw, int accumulate,
                          void* ws, size_t ws_bytes, void* stream) {
   (void)ws; (void)ws_bytes;
-  if (accumulate != 0 && accumulate != 1) return FP8BLK_INVALID_ARG;
-  if (M < 0) return FP8BLK_INVALID_ARG;
-  const int64_t mpad = (M + 127) / 128 * 128;
-  const int out = accumulate ? OUT_F32_ACC : OUT_F32;
-  // C = dW [N, K]: rows I = N, columns J = K, contraction L = M_pad.
-  if (N % 128 != 0) return FP8BLK_UNSUPPORTED_SHAPE;
-  const int rc = check_gemm(N, K, mpad, dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT, ld_sxT, true, dw,
-                            ld_dw, out, N);
-  if (rc == -1) return FP8BLK_OK;
-  if (rc != 0) return rc;
-  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  launch_block_gemm(dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT, ld_sxT, SB_ROWS, N, K, mpad, dw, ld_dw, out, 0,
-                    static_cast<hipStream_t>(stream));
-  return finish();
+  return gemm_impl(FP8BLK_OP_WGRAD, FP8BLK_GEMM_EXACT_BLOCKS, dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT,
+                   ld_sxT, M, N, K, dw, ld_dw, FP8BLK_OUT_F32, accumulate, static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+                   const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
+                   int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, int accumulate,
+                   void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  return gemm_impl(op, flags, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, M, N, K, c, ld_c, c_dtype, accumulate,
+                   static_cast<hipStream_t>(stream));
 }
 
 size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {

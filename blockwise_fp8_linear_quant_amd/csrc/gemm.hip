@@ -1,4 +1,4 @@
-// Block-scaled E4M3 GEMM for gfx950 (CDNA4 FP8 MFMA).
+// Block-scaled E4M3 GEMM for gfx950 (CDNA4 matrix cores).
 //
 // Pages: paperlayer.ai summary of arXiv 2608.27370v1, appendix C
 // "生産学習の詳細", item "FP8実装pipeline" -- the forward, data-gradient and
@@ -16,21 +16,23 @@
 //     wgrad    C = dW [N, K]: A = dYqT [N, M],  B = XqT [K, M]   (SB per row)
 //
 // gfx950 design:
-//   * one 128-wide scale block is multiplied per step: either by four
-//     v_mfma_f32_16x16x32_f16 on operands converted exactly from E4M3 to F16
-//     in registers (PREC_F16, whose block partial is the exact sum up to FP32
-//     rounding), or by one v_mfma_f32_16x16x128_f8f6f4 (PREC_FP8, faster, but
-//     the matrix core truncates small products inside groups of 8 -- see Prec);
-//   * each block partial of a 16x16 sub-tile starts from zero and is folded
-//     into an FP32 register accumulator with one FMA per element and block:
-//     acc = fma(P_lb, SA*SB, acc);
-//   * operand tiles stay E4M3 in HBM and LDS (1 byte per element), staged in
-//     128-byte rows (one K block) with an XOR swizzle of the 16-byte chunks so
-//     that fragment reads are bank-conflict free; global loads for block lb+1
-//     are in flight while block lb is multiplied (double-buffered LDS, one
-//     barrier per block);
-//   * workgroups are renumbered so that each of the 8 XCDs (own L2) works on
-//     a contiguous range of output tiles, grouped 8 tile-rows at a time.
+//   * operands stay E4M3 in HBM and LDS (one byte per element); each
+//     workgroup stages a BM x 128 tile of A and a BN x 128 tile of B per
+//     scale block with global_load_lds_dwordx4 (no VGPR round trip), double
+//     buffered so block lb+1 streams in while block lb is multiplied; rows
+//     are 128 bytes with the 16-byte chunks XOR-swizzled by (row % 8) so the
+//     ds_read_b128 fragment reads are bank-conflict free;
+//   * the block product of a 16x16 sub-tile is formed in the matrix core from
+//     a zero accumulator -- either four v_mfma_f32_16x16x32_f16 on operands
+//     converted exactly from E4M3 to F16 in registers (PREC_F16: the block
+//     partial is the exact sum up to FP32 rounding), or one
+//     v_mfma_f32_16x16x128_f8f6f4 (PREC_FP8: twice the matrix rate, but the
+//     hardware truncates small products inside groups of 8, see Prec) -- and
+//     folded into FP32 accumulators with one FMA per element and block;
+//   * the scales of block lb+1 (rows of A, and rows of B for the weight
+//     gradient) are staged into LDS alongside the operand tiles;
+//   * workgroups are renumbered so that each of the 8 XCDs (own L2) works on a
+//     contiguous range of output tiles, grouped 8 tile-rows at a time.
 #include "internal.h"
 #include "fp8_codec.h"
 
@@ -42,9 +44,28 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) void* gbl_void_t;
 
-// Four E4M3 codes (one dword) -> four F16 values, exact (every E4M3 value is an
-// F16 normal or zero).
+constexpr int BK = 128;
+constexpr int kThreads = 256;
+constexpr int kGroupM = 8;
+
+// PREC selects how the 128-term block product is formed:
+//   PREC_F16: the E4M3 codes are converted exactly to F16 in registers
+//     (v_cvt_scalef32_pk_f16_fp8 with scale 1; every E4M3 value is an F16
+//     normal or zero) and multiplied with v_mfma_f32_16x16x32_f16, four per
+//     block.  The matrix core adds the products of one instruction without
+//     intermediate truncation, so the block partial carries only FP32
+//     rounding (a few 2^-24 relative).
+//   PREC_FP8: one v_mfma_f32_16x16x128_f8f6f4 per block.  On gfx950 this
+//     instruction sums products in groups of 8 after aligning them to the
+//     largest product of the group and truncating 13 bits below it, so a block
+//     partial can be off by up to about 7 * 2^-13 of the group's largest
+//     product when values inside a group differ widely in magnitude.
+enum Prec { PREC_F16 = 0, PREC_FP8 = 1 };
+
+// Four E4M3 codes (one dword) -> four F16 values of an operand, exact.
 __device__ __forceinline__ void cvt4(uint32_t w, v8h& out, int half) {
   const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
   const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
@@ -54,18 +75,13 @@ __device__ __forceinline__ void cvt4(uint32_t w, v8h& out, int half) {
   out[4 * half + 3] = hi[1];
 }
 
-// 32 codes of a fragment (lane's K range of one 128-wide block) -> 4 F16
-// operands of 8 values, chunk c holding codes 8c..8c+7.
+// A lane's 32 codes of one block -> four F16 MFMA operands (chunk c = codes 8c..8c+7).
 __device__ __forceinline__ void cvt_frag(const uint4& lo, const uint4& hi, v8h (&f)[4]) {
   cvt4(lo.x, f[0], 0); cvt4(lo.y, f[0], 1);
   cvt4(lo.z, f[1], 0); cvt4(lo.w, f[1], 1);
   cvt4(hi.x, f[2], 0); cvt4(hi.y, f[2], 1);
   cvt4(hi.z, f[3], 0); cvt4(hi.w, f[3], 1);
 }
-
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kThreads = 256;
-constexpr int kGroupM = 8;
 
 __device__ __forceinline__ void map_tile(int pid, int nblocks, int tilesM, int tilesN, int& tm, int& tn) {
   // Workgroup pid runs on XCD pid % 8; give each XCD a contiguous logical range.
@@ -82,177 +98,189 @@ __device__ __forceinline__ void map_tile(int pid, int nblocks, int tilesM, int t
   tn = in_group / gm;
 }
 
+// Byte offset of 16-byte chunk `chunk` of tile row `row` in LDS.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
 
-// PREC selects how the exact 128-term block product is formed:
-//   PREC_F16: the E4M3 codes are converted exactly to F16 in registers and
-//     multiplied with v_mfma_f32_16x16x32_f16 (4 per block); the matrix core
-//     adds the products of one instruction without intermediate truncation, so
-//     each block partial carries only FP32 rounding (a few 2^-24 relative);
-//   PREC_FP8: one v_mfma_f32_16x16x128_f8f6f4 per block.  On gfx950 this
-//     instruction sums products in groups of 8 after aligning them to the
-//     largest product of the group and truncating below 2^-13 of it, so a block
-//     partial can be off by up to about 7 * 2^-13 of the group's largest
-//     product when values inside a group differ widely in magnitude.
-enum Prec { PREC_F16 = 0, PREC_FP8 = 1 };
+// Stage rows [0, ROWS) of a tile (row r = global row r0 + r, clamped to rmax)
+// for scale block lb into LDS at `dst`.  One wave instruction moves 8 rows
+// (1 KB); lane L writes LDS bytes [16L, 16L+16) of its instruction's 1 KB,
+// i.e. row 8u + L/8, slot L%8, which must hold global chunk (L%8) ^ (L/8).
+// Clamped rows (beyond the last valid row) only feed output rows that are
+// never stored.
+template <int ROWS>
+__device__ __forceinline__ void stage(const uint8_t* __restrict__ G, int64_t ld, int64_t r0, int64_t rmax,
+                                      int lb, uint8_t* dst, int wave, int lane) {
+#pragma unroll
+  for (int u = wave; u < ROWS / 8; u += 4) {
+    int64_t row = r0 + 8 * u + (lane >> 3);
+    row = row < rmax ? row : rmax;
+    const int chunk = (lane & 7) ^ (lane >> 3);
+    const uint8_t* src = G + row * ld + (int64_t)lb * BK + chunk * 16;
+    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(dst + u * 1024), 16, 0, 0);
+  }
+}
 
-template <int SB_MODE, int OUT, int PREC>
-__global__ __launch_bounds__(kThreads, 2) void block_gemm_kernel(
+__device__ __forceinline__ void frag_codes(const uint8_t* tile, int row, int ch, uint4& lo, uint4& hi) {
+  lo = *reinterpret_cast<const uint4*>(tile + swz(row, ch));
+  hi = *reinterpret_cast<const uint4*>(tile + swz(row, ch + 1));
+}
+
+// Stage N scale values SC[lb * ld + r0 + r], r < N (indices clamped to rmax),
+// into LDS at dst with 4-byte direct loads: one wave instruction moves 64.
+template <int N>
+__device__ __forceinline__ void stage_scales(const float* __restrict__ SC, int64_t ld, int64_t r0, int64_t rmax,
+                                             int lb, float* dst, int wave, int lane, int first_wave) {
+#pragma unroll
+  for (int u = 0; u < N / 64; ++u) {
+    if (wave == (first_wave + u) % 4) {
+      int64_t r = r0 + 64 * u + lane;
+      r = r < rmax ? r : rmax;
+      const float* src = SC + (int64_t)lb * ld + r;
+      __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(dst + 64 * u), 4, 0, 0);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC>
+__global__ __launch_bounds__(kThreads, (BM + BN) * BK * 2 <= 80 * 1024 ? 2 : 1) void block_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
     int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * BK];
+  constexpr int WGM = BM / WM, WGN = BN / WN;
+  static_assert(WGM * WGN == 4, "four waves per workgroup");
+  constexpr int MI = WM / 16, NI = WN / 16;
+  // Per buffer: A tile, B tile, BM row scales of A, BN row scales of B (SB_ROWS).
+  constexpr int kSaOff = (BM + BN) * BK;
+  constexpr int kSbOff = kSaOff + BM * 4;
+  constexpr int kBufBytes = kSbOff + (SB_MODE == SB_ROWS ? BN * 4 : 0);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int tm, tn;
   map_tile(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
-  const int wm = wave >> 1, wn = wave & 1;          // 2 x 2 waves, 64 x 64 each
+  const int wm = wave / WGN, wn = wave % WGN;
   const int nLB = (int)(L / BK);
+  const int64_t last_row = I - 1;
 
-  // Global -> LDS staging: thread t moves rows (t/8) + 32k, 16-byte chunk t%8.
-  const int lrow = t >> 3, lchunk = t & 7;
-  uint4 ra[4], rb[4];
-  auto gload = [&](int lb) {
+  v4f acc[MI][NI];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t r = i0 + lrow + 32 * k;
-      ra[k] = (r < I) ? *reinterpret_cast<const uint4*>(A + r * lda + (int64_t)lb * BK + lchunk * 16)
-                      : make_uint4(0, 0, 0, 0);
-      rb[k] = *reinterpret_cast<const uint4*>(B + (j0 + lrow + 32 * k) * ldb + (int64_t)lb * BK + lchunk * 16);
-    }
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // This lane's outputs in sub-tile (mi, ni): rows rbase + 16 mi + r (r < 4), column cbase + 16 ni.
+  const int64_t rbase = i0 + wm * WM + (lane >> 4) * 4;
+  const int64_t cbase = j0 + wn * WN + (lane & 15);
+
+  auto stage_all = [&](int lb, uint8_t* buf) {
+    stage<BM>(A, lda, i0, last_row, lb, buf, wave, lane);
+    stage<BN>(B, ldb, j0, j0 + BN - 1, lb, buf + BM * BK, wave, lane);
+    stage_scales<BM>(SA, ldsa, i0, last_row, lb, reinterpret_cast<float*>(buf + kSaOff), wave, lane, 0);
+    if (SB_MODE == SB_ROWS)
+      stage_scales<BN>(SB, ldsb, j0, j0 + BN - 1, lb, reinterpret_cast<float*>(buf + kSbOff), wave, lane,
+                       BM / 64);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int off = swz(lrow + 32 * k, lchunk);
-      *reinterpret_cast<uint4*>(&lds_a[buf][off]) = ra[k];
-      *reinterpret_cast<uint4*>(&lds_b[buf][off]) = rb[k];
-    }
-  };
 
-  v4f acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // Rows of this lane's outputs in sub-tile mi: rbase + mi*16 + r, r = 0..3.
-  const int64_t rbase = i0 + wm * 64 + (lane >> 4) * 4;
-  const int64_t cbase = j0 + wn * 64 + (lane & 15);
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  lstore(0);
+  stage_all(0, lds);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  const int ch = (lane >> 4) * 2;
   for (int lb = 0; lb < nLB; ++lb) {
-    const int buf = lb & 1;
-    if (lb + 1 < nLB) gload(lb + 1);
+    uint8_t* cur = lds + (lb & 1) * kBufBytes;
+    const uint8_t* ta = cur;
+    const uint8_t* tb = cur + BM * BK;
+    if (lb + 1 < nLB) stage_all(lb + 1, lds + ((lb + 1) & 1) * kBufBytes);
 
-    // Scales of this block.
-    float sa[4][4];
+    // Scales of this block: rows of A from LDS; B's block scale (fwd/dgrad)
+    // is uniform over the tile and folded into the row scales.
+    float sa[MI][4], sb[NI];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int64_t row = rbase + mi * 16;
-      const float* p = SA + (int64_t)lb * ldsa + row;
-      if (row + 4 <= I) {
-        const float4 v = *reinterpret_cast<const float4*>(p);
-        sa[mi][0] = v.x; sa[mi][1] = v.y; sa[mi][2] = v.z; sa[mi][3] = v.w;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sa[mi][r] = (row + r < I) ? p[r] : 0.0f;
-      }
+    for (int mi = 0; mi < MI; ++mi) {
+      const float4 v = *reinterpret_cast<const float4*>(cur + kSaOff + (wm * WM + mi * 16 + (lane >> 4) * 4) * 4);
+      sa[mi][0] = v.x; sa[mi][1] = v.y; sa[mi][2] = v.z; sa[mi][3] = v.w;
     }
-    float sb[4];
     if (SB_MODE == SB_BLOCK) {
       const float s = SB[(j0 / 128) * nLB + lb];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sa[mi][r] *= s;
     } else {
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) sb[ni] = SB[(int64_t)lb * ldsb + cbase + ni * 16];
+      for (int ni = 0; ni < NI; ++ni)
+        sb[ni] = reinterpret_cast<const float*>(cur + kSbOff)[wn * WN + ni * 16 + (lane & 15)];
     }
 
-    // Fragments: lane holds row (lane%16) of a 16-row sub-tile, 32 K-bytes
-    // starting at 32*(lane/16); A and B use the same K arrangement, so the
-    // order in which the MFMA pairs K elements does not matter.
-    const int ch = (lane >> 4) * 2;
     if (PREC == PREC_FP8) {
-      v8i fa[4], fb[4];
+      v8i fa[MI];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int row = wm * 64 + mi * 16 + (lane & 15);
-        const uint4 lo = *reinterpret_cast<const uint4*>(&lds_a[buf][swz(row, ch)]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&lds_a[buf][swz(row, ch + 1)]);
+      for (int mi = 0; mi < MI; ++mi) {
+        uint4 lo, hi;
+        frag_codes(ta, wm * WM + mi * 16 + (lane & 15), ch, lo, hi);
         fa[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int row = wn * 64 + ni * 16 + (lane & 15);
-        const uint4 lo = *reinterpret_cast<const uint4*>(&lds_b[buf][swz(row, ch)]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&lds_b[buf][swz(row, ch + 1)]);
-        fb[ni] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+      for (int ni = 0; ni < NI; ++ni) {
+        uint4 lo, hi;
+        frag_codes(tb, wn * WN + ni * 16 + (lane & 15), ch, lo, hi);
+        const v8i fb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          // E4M3 x E4M3 (format selectors 0, 0), no block scaling in the MFMA.
-          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[mi], fb[ni], zero, 0, 0, 0, 0, 0, 0);
+        for (int mi = 0; mi < MI; ++mi) {
+          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[mi], fb, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float s = (SB_MODE == SB_BLOCK) ? sa[mi][r] : sa[mi][r] * sb[ni];
             acc[mi][ni][r] = fmaf(p[r], s, acc[mi][ni][r]);
           }
         }
+        // Keep at most one column of partials live (register budget).
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      v8h fb[4][4];
+      v8h fa[MI][4];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int row = wn * 64 + ni * 16 + (lane & 15);
-        const uint4 lo = *reinterpret_cast<const uint4*>(&lds_b[buf][swz(row, ch)]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&lds_b[buf][swz(row, ch + 1)]);
-        cvt_frag(lo, hi, fb[ni]);
+      for (int mi = 0; mi < MI; ++mi) {
+        uint4 lo, hi;
+        frag_codes(ta, wm * WM + mi * 16 + (lane & 15), ch, lo, hi);
+        cvt_frag(lo, hi, fa[mi]);
       }
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int row = wm * 64 + mi * 16 + (lane & 15);
-        const uint4 lo = *reinterpret_cast<const uint4*>(&lds_a[buf][swz(row, ch)]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&lds_a[buf][swz(row, ch + 1)]);
-        v8h fa[4];
-        cvt_frag(lo, hi, fa);
+      for (int ni = 0; ni < NI; ++ni) {
+        uint4 lo, hi;
+        frag_codes(tb, wn * WN + ni * 16 + (lane & 15), ch, lo, hi);
+        v8h fb[4];
+        cvt_frag(lo, hi, fb);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          v4f p = zero;
+        for (int mi = 0; mi < MI; ++mi) {
+          v4f p = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < 4; ++c) p = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[c], fb[ni][c], p, 0, 0, 0);
+          for (int c = 0; c < 4; ++c) p = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[mi][c], fb[c], p, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float s = (SB_MODE == SB_BLOCK) ? sa[mi][r] : sa[mi][r] * sb[ni];
             acc[mi][ni][r] = fmaf(p[r], s, acc[mi][ni][r]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    if (lb + 1 < nLB) lstore(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's staging of block lb+1 has landed
+    __syncthreads();                  // ... and everyone's; block lb is no longer read
   }
 
-  // Epilogue: lane owns rows rbase + mi*16 + r, column cbase + ni*16.
+  // Epilogue: lane owns rows rbase + 16 mi + r, columns cbase + 16 ni.
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t row = rbase + mi * 16 + r;
       if (row >= I) continue;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
         const int64_t col = cbase + ni * 16;
         const float v = acc[mi][ni][r];
         if (OUT == OUT_F32) {
@@ -278,17 +306,20 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void* __restrict__ C, in
   }
 }
 
-template <int SB_MODE, int OUT>
-void launch_t(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
-              const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
-              int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int prec, hipStream_t st) {
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC>
+void launch_cfg(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
+                const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
+                int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
   const int tilesM = (int)((I + BM - 1) / BM), tilesN = (int)(J / BN);
-  if (prec == PREC_FP8)
-    hipLaunchKernelGGL((block_gemm_kernel<SB_MODE, OUT, PREC_FP8>), dim3(tilesM * tilesN), dim3(kThreads), 0, st,
-                       A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
-  else
-    hipLaunchKernelGGL((block_gemm_kernel<SB_MODE, OUT, PREC_F16>), dim3(tilesM * tilesN), dim3(kThreads), 0, st,
-                       A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+  hipLaunchKernelGGL((block_gemm_kernel<BM, BN, WM, WN, SB_MODE, OUT, PREC>), dim3(tilesM * tilesN),
+                     dim3(kThreads), 0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+}
+
+template <int SB_MODE, int OUT, int PREC>
+void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
+                 const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
+                 int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
+  launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
 }
 
 }  // namespace
@@ -307,10 +338,13 @@ void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t l
       hipLaunchKernelGGL(fill_zero_kernel<OUT_F32>, dim3(blocks), dim3(256), 0, st, C, I, J, ldc);
     return;
   }
-#define FP8BLK_GEMM_CASE(SBM, OM)                                                    \
-  if (sb_mode == SBM && out_mode == OM) {                                            \
-    launch_t<SBM, OM>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, prec, st);      \
-    return;                                                                          \
+#define FP8BLK_GEMM_CASE(SBM, OM)                                                              \
+  if (sb_mode == SBM && out_mode == OM) {                                                      \
+    if (prec == PREC_FP8)                                                                      \
+      launch_prec<SBM, OM, PREC_FP8>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st); \
+    else                                                                                       \
+      launch_prec<SBM, OM, PREC_F16>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st); \
+    return;                                                                                    \
   }
   FP8BLK_GEMM_CASE(SB_BLOCK, OUT_F32)
   FP8BLK_GEMM_CASE(SB_BLOCK, OUT_BF16)

@@ -98,3 +98,17 @@ def test_binding_raises_without_library(tmp_path):
             L.load(str(tmp_path / "missing.so"))
     finally:
         L._lib = saved
+
+
+def test_generic_gemm_validation():
+    lib = _lib()
+    P = ctypes.c_void_p(16)
+    # bad op, bad flags, accumulate on a forward, BF16 weight gradient
+    assert lib.fp8_block_gemm(7, 0, P, 256, P, 16, P, 256, P, 0, 16, 256, 256, P, 256, 0, 0, None, 0, None) == 1
+    assert lib.fp8_block_gemm(0, 5, P, 256, P, 16, P, 256, P, 0, 16, 256, 256, P, 256, 0, 0, None, 0, None) == 1
+    assert lib.fp8_block_gemm(0, 1, P, 256, P, 16, P, 256, P, 0, 16, 256, 256, P, 256, 0, 1, None, 0, None) == 1
+    assert lib.fp8_block_gemm(2, 1, P, 256, P, 16, P, 256, P, 256, 16, 256, 256, P, 256, 1, 0, None, 0, None) == 1
+    # shape rules are those of the named calls
+    assert lib.fp8_block_gemm(0, 1, P, 256, P, 16, P, 256, P, 0, 16, 200, 256, P, 256, 0, 0, None, 0, None) == 2
+    assert lib.fp8_block_gemm(0, 1, None, 0, None, 0, None, 0, None, 0, 0, 256, 256, None, 0, 0, 0, None, 0,
+                              None) == 0

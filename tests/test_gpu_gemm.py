@@ -300,3 +300,93 @@ def test_every_code_through_both_operands(B):
     dw = e4m3.decode(wq).astype(np.float64)
     ref = dx @ dw.T
     assert np.array_equal(y.astype(np.float64), ref)
+
+
+# --- the FP8 matrix-core path (fp8_block_gemm with FP8BLK_GEMM_FP8_MATRIX_CORE) ---
+# Its block products carry the hardware's in-group truncation: at most 7 of 8
+# products of a group lose bits below 2^-13 of the group's largest product, so
+# per block |err| <= 7 * 2^-13 * sum|p| and overall |err| <= 2^-10 * sum|a*b|
+# plus the FP32 accumulation term.  On Gaussian operands it also meets the
+# exact-block tolerance, which is checked where it holds.
+FP8_PATH_RTOL = 2.0 ** -10 + 1e-5
+
+
+class FastLayer(Layer):
+    def fwd(self, out_dtype):
+        B = self.B
+        xq, sx = B.fp8_quant_1x128(self.x)
+        wq, sw, _, _ = B.fp8_quant_128x128(self.w)
+        y = B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=out_dtype, fp8_matrix_core=True)
+        oxq, osx = quant.quant_1x128_rows(self.xb)
+        owq, osw = quant.quant_128x128(self.wb)
+        return host(y), (lambda rows=None, cols=None: gemm.fwd(oxq, osx, owq, osw, rows, cols))
+
+    def dgrad(self, out_dtype):
+        B = self.B
+        dyq, sdy = B.fp8_quant_1x128(self.dy)
+        _, _, wqT, swT = B.fp8_quant_128x128(self.w, with_transpose=True)
+        dx = B.fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=out_dtype, fp8_matrix_core=True)
+        odyq, osdy = quant.quant_1x128_rows(self.dyb)
+        owqT, oswT = quant.quant_128x128(np.ascontiguousarray(self.wb.T))
+        return host(dx), (lambda rows=None, cols=None: gemm.dgrad(odyq, osdy, owqT, oswT, rows, cols))
+
+    def wgrad(self, accumulate=False, dw0=None):
+        B = self.B
+        dyqT, sdyT = B.fp8_quant_1x128(self.dy, transpose_out=True)
+        xqT, sxT = B.fp8_quant_1x128(self.x, transpose_out=True)
+        dw = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=self.M, fp8_matrix_core=True)
+        odyqT, osdyT = quant.quant_1x128_tokens(self.dyb)
+        oxqT, osxT = quant.quant_1x128_tokens(self.xb)
+        return host(dw), (lambda rows=None, cols=None: gemm.wgrad(odyqT, osdyT, oxqT, osxT, rows, cols))
+
+
+def _check_fp32_rtol(got, ref_fn, rtol, label, rng=None, k=40):
+    if rng is None:
+        y, bnd = ref_fn()
+        ok, rep = compare.check_fp32(got, y, bnd, rtol=rtol)
+        assert ok, f"{label}: {rep}"
+        return
+    I, J = got.shape
+    rows = sample_index(I, k, rng, must=(0, I - 1))
+    y, bnd = ref_fn(rows, None)
+    ok, rep = compare.check_fp32(got[rows], y, bnd, rtol=rtol)
+    assert ok, f"{label}: {rep}"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 384, 256), (1000, 256, 1024)])
+def test_fp8_matrix_core_small_gaussian(B, M, N, K):
+    torch = _torch()
+    xb = W.normal_bf16((M, K), 1.0, W.seed_for(93, M, 0, "x"))
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(93, M, 0, "w"))
+    dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(93, M, 0, "dy"))
+    L = FastLayer(B, xb, wb, dyb)
+    say("fp8 path fwd/dgrad/wgrad", (M, N, K))
+    got, ref = L.fwd(torch.float32)
+    _check_fp32_rtol(got, ref, FP8_PATH_RTOL, "fp8 fwd")
+    got, ref = L.dgrad(torch.float32)
+    _check_fp32_rtol(got, ref, FP8_PATH_RTOL, "fp8 dgrad")
+    got, ref = L.wgrad()
+    _check_fp32_rtol(got, ref, FP8_PATH_RTOL, "fp8 wgrad")
+
+
+def test_fp8_matrix_core_config1_exact_tolerance(B):
+    """On configuration 1 (Gaussian) the FP8 path also meets the exact-block tolerance."""
+    torch = _torch()
+    xb = W.normal_bf16((256, 2048), 1.0, W.seed_for(1, 0, "o", "x"))
+    wb = W.normal_bf16((2048, 2048), 0.02, W.seed_for(1, 0, "o", "w"))
+    L = FastLayer(B, xb, wb, None)
+    say("fp8 path cfg1")
+    got, ref = L.fwd(torch.float32)
+    check_full(got, ref, "f32", "fp8 path cfg1")
+
+
+def test_fp8_matrix_core_stress_M3000(B):
+    """Configuration 5 on the FP8 path: within the derived in-group truncation bound."""
+    xb = W.student_t_stress((3000, 6144), W.seed_for(5, 0, "down", "x"))
+    wb = W.normal_bf16((2048, 6144), 0.02, W.seed_for(5, 0, "down", "w"))
+    dyb = W.normal_bf16((3000, 2048), 1e-3, W.seed_for(5, 0, "down", "dy"))
+    L = FastLayer(B, xb, wb, dyb)
+    rng = np.random.default_rng(55)
+    say("fp8 path cfg5 wgrad")
+    got, ref = L.wgrad()
+    _check_fp32_rtol(got, ref, FP8_PATH_RTOL, "fp8 cfg5 wgrad", rng)
