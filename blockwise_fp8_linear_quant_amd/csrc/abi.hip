@@ -46,6 +46,8 @@ int check_gemm(int64_t I, int64_t J, int64_t L, const void* A, int64_t lda, cons
   if (L == 0) return 0;
   if (A == nullptr || B == nullptr || SA == nullptr || SB == nullptr) return FP8BLK_INVALID_ARG;
   if (lda < L || ldb < L || ldsa < L_valid_rows_sa) return FP8BLK_INVALID_ARG;
+  // The kernels address operand rows with 32-bit byte offsets.
+  if (I * lda >= (int64_t)1 << 31 || J * ldb >= (int64_t)1 << 31) return FP8BLK_UNSUPPORTED_SHAPE;
   if (sb_rows && ldsb < J) return FP8BLK_INVALID_ARG;
   if (!al16(A) || !al16(B) || lda % 16 != 0 || ldb % 16 != 0) return FP8BLK_MISALIGNED;
   if (!al16(SA) || ldsa % 4 != 0) return FP8BLK_MISALIGNED;

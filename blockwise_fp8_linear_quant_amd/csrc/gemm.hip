@@ -17,20 +17,25 @@
 //
 // gfx950 design:
 //   * operands stay E4M3 in HBM and LDS (one byte per element); each
-//     workgroup stages a BM x 128 tile of A and a BN x 128 tile of B per
-//     scale block with global_load_lds_dwordx4 (no VGPR round trip), double
-//     buffered so block lb+1 streams in while block lb is multiplied; rows
-//     are 128 bytes with the 16-byte chunks XOR-swizzled by (row % 8) so the
-//     ds_read_b128 fragment reads are bank-conflict free;
-//   * the block product of a 16x16 sub-tile is formed in the matrix core from
-//     a zero accumulator -- either four v_mfma_f32_16x16x32_f16 on operands
-//     converted exactly from E4M3 to F16 in registers (PREC_F16: the block
-//     partial is the exact sum up to FP32 rounding), or one
-//     v_mfma_f32_16x16x128_f8f6f4 (PREC_FP8: twice the matrix rate, but the
-//     hardware truncates small products inside groups of 8, see Prec) -- and
-//     folded into FP32 accumulators with one FMA per element and block;
-//   * the scales of block lb+1 (rows of A, and rows of B for the weight
-//     gradient) are staged into LDS alongside the operand tiles;
+//     workgroup stages a BM x 128 tile of A, a BN x 128 tile of B and their
+//     per-row scales per scale block with global_load_lds (no VGPR round
+//     trip) into one of several LDS buffers, so block lb+1 streams in while block
+//     lb is multiplied (large problems: three buffers, block lb+2 in flight).
+//     The buffers are distinct LDS objects and the block loop is unrolled by
+//     the buffer count, which lets the compiler see that reads of one buffer
+//     never wait for the fill of another.  Rows are 128 bytes with
+//     the 16-byte chunks XOR-swizzled by (row % 8), so fragment reads
+//     (ds_read_b128) are bank-conflict free;
+//   * the block product of a sub-tile is formed in the matrix core from a zero
+//     accumulator and folded into FP32 register accumulators with one FMA per
+//     element and block (acc = fma(P_lb, SA*SB, acc)):
+//       PREC_F16 (default, exact): E4M3 codes are converted exactly to F16 in
+//         registers and multiplied with v_mfma_f32_32x32x16_f16, eight per
+//         32x32 sub-tile and block (the 32x32 shape sustains ~2.1 PF on
+//         MI355X, the 16x16x32 shape about half of that);
+//       PREC_FP8: one v_mfma_f32_16x16x128_f8f6f4 per 16x16 sub-tile and
+//         block (twice the matrix rate, but the hardware truncates small
+//         products inside groups of 8, see Prec);
 //   * workgroups are renumbered so that each of the 8 XCDs (own L2) works on a
 //     contiguous range of output tiles, grouped 8 tile-rows at a time.
 #include "internal.h"
@@ -42,22 +47,27 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 constexpr int BK = 128;
-constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained; gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
 
 // PREC selects how the 128-term block product is formed:
 //   PREC_F16: the E4M3 codes are converted exactly to F16 in registers
 //     (v_cvt_scalef32_pk_f16_fp8 with scale 1; every E4M3 value is an F16
-//     normal or zero) and multiplied with v_mfma_f32_16x16x32_f16, four per
-//     block.  The matrix core adds the products of one instruction without
-//     intermediate truncation, so the block partial carries only FP32
-//     rounding (a few 2^-24 relative).
+//     normal or zero) and multiplied with v_mfma_f32_32x32x16_f16.  The
+//     matrix core adds the products of one instruction without intermediate
+//     truncation, so the block partial carries only FP32 rounding (a few
+//     2^-24 relative).
 //   PREC_FP8: one v_mfma_f32_16x16x128_f8f6f4 per block.  On gfx950 this
 //     instruction sums products in groups of 8 after aligning them to the
 //     largest product of the group and truncating 13 bits below it, so a block
@@ -65,22 +75,13 @@ constexpr int kGroupM = 8;
 //     product when values inside a group differ widely in magnitude.
 enum Prec { PREC_F16 = 0, PREC_FP8 = 1 };
 
-// Four E4M3 codes (one dword) -> four F16 values of an operand, exact.
-__device__ __forceinline__ void cvt4(uint32_t w, v8h& out, int half) {
-  const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-  const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
-  out[4 * half + 0] = lo[0];
-  out[4 * half + 1] = lo[1];
-  out[4 * half + 2] = hi[0];
-  out[4 * half + 3] = hi[1];
-}
-
-// A lane's 32 codes of one block -> four F16 MFMA operands (chunk c = codes 8c..8c+7).
-__device__ __forceinline__ void cvt_frag(const uint4& lo, const uint4& hi, v8h (&f)[4]) {
-  cvt4(lo.x, f[0], 0); cvt4(lo.y, f[0], 1);
-  cvt4(lo.z, f[1], 0); cvt4(lo.w, f[1], 1);
-  cvt4(hi.x, f[2], 0); cvt4(hi.y, f[2], 1);
-  cvt4(hi.z, f[3], 0); cvt4(hi.w, f[3], 1);
+// Eight E4M3 codes (two dwords) -> one F16 MFMA operand, exact.
+__device__ __forceinline__ v8h cvt8(uint32_t w0, uint32_t w1) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 __device__ __forceinline__ void map_tile(int pid, int nblocks, int tilesM, int tilesN, int& tm, int& tn) {
@@ -101,188 +102,266 @@ __device__ __forceinline__ void map_tile(int pid, int nblocks, int tilesM, int t
 // Byte offset of 16-byte chunk `chunk` of tile row `row` in LDS.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
 
-// Stage rows [0, ROWS) of a tile (row r = global row r0 + r, clamped to rmax)
-// for scale block lb into LDS at `dst`.  One wave instruction moves 8 rows
-// (1 KB); lane L writes LDS bytes [16L, 16L+16) of its instruction's 1 KB,
-// i.e. row 8u + L/8, slot L%8, which must hold global chunk (L%8) ^ (L/8).
-// Clamped rows (beyond the last valid row) only feed output rows that are
-// never stored.
-template <int ROWS>
-__device__ __forceinline__ void stage(const uint8_t* __restrict__ G, int64_t ld, int64_t r0, int64_t rmax,
-                                      int lb, uint8_t* dst, int wave, int lane) {
-#pragma unroll
-  for (int u = wave; u < ROWS / 8; u += 4) {
-    int64_t row = r0 + 8 * u + (lane >> 3);
-    row = row < rmax ? row : rmax;
-    const int chunk = (lane & 7) ^ (lane >> 3);
-    const uint8_t* src = G + row * ld + (int64_t)lb * BK + chunk * 16;
-    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(dst + u * 1024), 16, 0, 0);
-  }
+__device__ __forceinline__ uint4 lds16(const uint8_t* tile, int row, int chunk) {
+  return *reinterpret_cast<const uint4*>(tile + swz(row, chunk));
 }
 
-__device__ __forceinline__ void frag_codes(const uint8_t* tile, int row, int ch, uint4& lo, uint4& hi) {
-  lo = *reinterpret_cast<const uint4*>(tile + swz(row, ch));
-  hi = *reinterpret_cast<const uint4*>(tile + swz(row, ch + 1));
-}
-
-// Stage N scale values SC[lb * ld + r0 + r], r < N (indices clamped to rmax),
-// into LDS at dst with 4-byte direct loads: one wave instruction moves 64.
-template <int N>
-__device__ __forceinline__ void stage_scales(const float* __restrict__ SC, int64_t ld, int64_t r0, int64_t rmax,
-                                             int lb, float* dst, int wave, int lane, int first_wave) {
+// Direct-to-LDS staging.  A tile of ROWS rows x 128 bytes moves with ROWS/8
+// wave instructions of 1 KB; lane L of instruction `blk` writes LDS bytes
+// [16L, 16L+16) of its 1 KB, i.e. tile row 8 blk + L/8, slot L%8, which must
+// hold global chunk (L%8) ^ (L/8) of that row.  The per-lane byte offsets of
+// the source rows are loop invariant (computed once, 32-bit: every operand
+// here is below 2 GiB); per scale block only the wave-uniform base pointer
+// moves, so each load is one instruction with no address arithmetic.  Rows
+// past the last valid row are clamped to it; they only feed output rows that
+// are never stored.
+template <int ROWS, int NW>
+struct TileStager {
+  static constexpr int kLoads = ROWS / (8 * NW);   // instructions per wave
+  static_assert(kLoads * 8 * NW == ROWS, "tile rows must split evenly over the waves");
+  uint32_t off[kLoads];
+  __device__ __forceinline__ void init(int64_t ld, int64_t r0, int64_t rmax, int wave, int lane) {
 #pragma unroll
-  for (int u = 0; u < N / 64; ++u) {
-    if (wave == (first_wave + u) % 4) {
-      int64_t r = r0 + 64 * u + lane;
-      r = r < rmax ? r : rmax;
-      const float* src = SC + (int64_t)lb * ld + r;
-      __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(dst + 64 * u), 4, 0, 0);
+    for (int u = 0; u < kLoads; ++u) {
+      int64_t row = r0 + 8 * (NW * u + wave) + (lane >> 3);
+      row = row < rmax ? row : rmax;
+      off[u] = (uint32_t)(row * ld) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
     }
   }
-}
+  // base: G + lb * 128 (wave-uniform); dst: the tile in LDS.
+  __device__ __forceinline__ void issue(const uint8_t* base, uint8_t* dst, int wave) const {
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u)
+      __builtin_amdgcn_global_load_lds((gbl_void_t)(base + off[u]), (lds_void_t)(dst + (NW * u + wave) * 1024), 16, 0, 0);
+  }
+};
 
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC>
-__global__ __launch_bounds__(kThreads, (BM + BN) * BK * 2 <= 80 * 1024 ? 2 : 1) void block_gemm_kernel(
+// N scale values SC[lb * ld + r0 + r] (indices clamped to rmax) into LDS with
+// 4-byte direct loads, N/NW per wave (one instruction each).
+template <int N, int NW>
+struct ScaleStager {
+  static constexpr int kPerWave = N / NW;
+  static_assert(kPerWave <= 64, "one instruction per wave");
+  uint32_t off;
+  __device__ __forceinline__ void init(int64_t r0, int64_t rmax, int wave, int lane) {
+    int64_t r = r0 + kPerWave * wave + (lane < kPerWave ? lane : 0);
+    r = r < rmax ? r : rmax;
+    off = (uint32_t)r * 4u;
+  }
+  // base: SC + lb * ld (wave-uniform).
+  __device__ __forceinline__ void issue(const float* base, float* dst, int wave, int lane) const {
+    if (lane < kPerWave)
+      __builtin_amdgcn_global_load_lds((gbl_void_t)(reinterpret_cast<const uint8_t*>(base) + off),
+                                       (lds_void_t)(dst + kPerWave * wave), 4, 0, 0);
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int SB_MODE, int PREC, int NW, int NS>
+struct Cfg {
+  static constexpr int WGM = BM / WM, WGN = BN / WN;
+  static_assert(WGM * WGN == NW, "one wave per WM x WN sub-tile");
+  static_assert(NS == 2 || NS == 3, "double or triple buffering");
+  // Vector-memory instructions one wave issues to stage one block.
+  static constexpr int kVmemPerBlock =
+      TileStager<BM, NW>::kLoads + TileStager<BN, NW>::kLoads + 1 + (SB_MODE == SB_ROWS ? 1 : 0);
+  // Sub-tile edge: 32 for the F16 path (32x32x16 MFMA), 16 for the FP8 path.
+  static constexpr int T = PREC == PREC_F16 ? 32 : 16;
+  static constexpr int MT = WM / T, NT = WN / T;
+  static constexpr int ACC = T * T / 64;          // accumulator floats per lane per sub-tile
+  // Per-buffer LDS layout: A tile, B tile, BM row scales of A, BN row scales of B (SB_ROWS).
+  static constexpr int kSaOff = (BM + BN) * BK;
+  static constexpr int kSbOff = kSaOff + BM * 4;
+  static constexpr int kBufBytes = kSbOff + (SB_MODE == SB_ROWS ? BN * 4 : 0);
+};
+
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
     int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
-  constexpr int WGM = BM / WM, WGN = BN / WN;
-  static_assert(WGM * WGN == 4, "four waves per workgroup");
-  constexpr int MI = WM / 16, NI = WN / 16;
-  // Per buffer: A tile, B tile, BM row scales of A, BN row scales of B (SB_ROWS).
-  constexpr int kSaOff = (BM + BN) * BK;
-  constexpr int kSbOff = kSaOff + BM * 4;
-  constexpr int kBufBytes = kSbOff + (SB_MODE == SB_ROWS ? BN * 4 : 0);
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
+  using C = Cfg<BM, BN, WM, WN, SB_MODE, PREC, NW, NS>;
+  constexpr int T = C::T, MT = C::MT, NT = C::NT, ACC = C::ACC;
+  // One distinct LDS object per pipeline stage (see the file comment).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[NS == 3 ? C::kBufBytes : 16];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   int tm, tn;
   map_tile(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int nLB = (int)(L / BK);
   const int64_t last_row = I - 1;
 
-  v4f acc[MI][NI];
+  float acc[MT][NT][ACC];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < ACC; ++e) acc[mt][nt][e] = 0.0f;
 
-  // This lane's outputs in sub-tile (mi, ni): rows rbase + 16 mi + r (r < 4), column cbase + 16 ni.
-  const int64_t rbase = i0 + wm * WM + (lane >> 4) * 4;
-  const int64_t cbase = j0 + wn * WN + (lane & 15);
-
+  TileStager<BM, NW> sta;
+  TileStager<BN, NW> stb;
+  ScaleStager<BM, NW> ssa;
+  ScaleStager<BN, NW> ssb;
+  sta.init(lda, i0, last_row, wave, lane);
+  stb.init(ldb, j0, j0 + BN - 1, wave, lane);
+  ssa.init(i0, last_row, wave, lane);
+  ssb.init(j0, j0 + BN - 1, wave, lane);
   auto stage_all = [&](int lb, uint8_t* buf) {
-    stage<BM>(A, lda, i0, last_row, lb, buf, wave, lane);
-    stage<BN>(B, ldb, j0, j0 + BN - 1, lb, buf + BM * BK, wave, lane);
-    stage_scales<BM>(SA, ldsa, i0, last_row, lb, reinterpret_cast<float*>(buf + kSaOff), wave, lane, 0);
-    if (SB_MODE == SB_ROWS)
-      stage_scales<BN>(SB, ldsb, j0, j0 + BN - 1, lb, reinterpret_cast<float*>(buf + kSbOff), wave, lane,
-                       BM / 64);
+    sta.issue(A + (int64_t)lb * BK, buf, wave);
+    stb.issue(B + (int64_t)lb * BK, buf + BM * BK, wave);
+    ssa.issue(SA + (int64_t)lb * ldsa, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
+    if (SB_MODE == SB_ROWS) ssb.issue(SB + (int64_t)lb * ldsb, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
   };
 
-  stage_all(0, lds);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  const int ch = (lane >> 4) * 2;
-  for (int lb = 0; lb < nLB; ++lb) {
-    uint8_t* cur = lds + (lb & 1) * kBufBytes;
+  // One scale block: start filling `nxt` with block lb + NS - 1, multiply
+  // block lb from `cur`, then wait until block lb + 1 has landed (the fill
+  // just issued may stay in flight) and synchronise.
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int lb) {
+    const bool fill = lb + NS - 1 < nLB;
+    if (fill) stage_all(lb + NS - 1, nxt);
     const uint8_t* ta = cur;
     const uint8_t* tb = cur + BM * BK;
-    if (lb + 1 < nLB) stage_all(lb + 1, lds + ((lb + 1) & 1) * kBufBytes);
+    const float* lsa = reinterpret_cast<const float*>(cur + C::kSaOff);
+    const float* lsb = reinterpret_cast<const float*>(cur + C::kSbOff);
+    const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLB + lb] : 1.0f;
 
-    // Scales of this block: rows of A from LDS; B's block scale (fwd/dgrad)
-    // is uniform over the tile and folded into the row scales.
-    float sa[MI][4], sb[NI];
+    if (PREC == PREC_F16) {
+      // 32x32 sub-tiles.  Lane l: row (l % 32) of the sub-tile, half h = l / 32
+      // holds K bytes [64h, 64h + 64) of the block; MFMA k (k < 8) takes the
+      // 8 codes at 64h + 8k.  Outputs: column l % 32, rows 8q + 4h + u for
+      // accumulator 4q + u.  The MT x NT sub-tile products are built side by
+      // side, two K slices (one 16-byte LDS read per row) at a time, so the
+      // matrix core always has independent accumulation chains.
+      const int h = lane >> 5, rr = lane & 31;
+      v16f p[MT][NT];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const float4 v = *reinterpret_cast<const float4*>(cur + kSaOff + (wm * WM + mi * 16 + (lane >> 4) * 4) * 4);
-      sa[mi][0] = v.x; sa[mi][1] = v.y; sa[mi][2] = v.z; sa[mi][3] = v.w;
-    }
-    if (SB_MODE == SB_BLOCK) {
-      const float s = SB[(j0 / 128) * nLB + lb];
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+        for (int nt = 0; nt < NT; ++nt) p[mt][nt] = v16f{};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sa[mi][r] *= s;
+      for (int c = 0; c < 4; ++c) {
+        v8h a[MT][2], b[NT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 v = lds16(ta, wm * WM + mt * 32 + rr, 4 * h + c);
+          a[mt][0] = cvt8(v.x, v.y);
+          a[mt][1] = cvt8(v.z, v.w);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint4 v = lds16(tb, wn * WN + nt * 32 + rr, 4 * h + c);
+          b[nt][0] = cvt8(v.x, v.y);
+          b[nt][1] = cvt8(v.z, v.w);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              p[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt][k], b[nt][k], p[mt][nt], 0, 0, 0);
+      }
+      // Rescale-accumulate.  Row scales of accumulator e: rows 8(e/4) + 4h + e%4.
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float sr[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(lsa + wm * WM + mt * 32 + 8 * q + 4 * h);
+          sr[4 * q + 0] = v.x * sblk; sr[4 * q + 1] = v.y * sblk;
+          sr[4 * q + 2] = v.z * sblk; sr[4 * q + 3] = v.w * sblk;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float sbc = (SB_MODE == SB_ROWS) ? lsb[wn * WN + nt * 32 + rr] : 1.0f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float sc = (SB_MODE == SB_ROWS) ? sr[e] * sbc : sr[e];
+            acc[mt][nt][e] = fmaf(p[mt][nt][e], sc, acc[mt][nt][e]);
+          }
+        }
+      }
     } else {
+      // 16x16 sub-tiles.  Lane l: row (l % 16), K bytes [32 (l / 16), +32).
+      // Outputs: column l % 16, rows 4 (l / 16) + u for accumulator u.
+      const int g = lane >> 4, rr = lane & 15;
+      v8i fa[MT];
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        sb[ni] = reinterpret_cast<const float*>(cur + kSbOff)[wn * WN + ni * 16 + (lane & 15)];
-    }
-
-    if (PREC == PREC_FP8) {
-      v8i fa[MI];
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * WM + mt * 16 + rr;
+        const uint4 lo = lds16(ta, row, 2 * g), hi = lds16(ta, row, 2 * g + 1);
+        fa[mt] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      float s[MT][4];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        uint4 lo, hi;
-        frag_codes(ta, wm * WM + mi * 16 + (lane & 15), ch, lo, hi);
-        fa[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int mt = 0; mt < MT; ++mt) {
+        const float4 v = *reinterpret_cast<const float4*>(lsa + wm * WM + mt * 16 + 4 * g);
+        s[mt][0] = v.x * sblk; s[mt][1] = v.y * sblk; s[mt][2] = v.z * sblk; s[mt][3] = v.w * sblk;
       }
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        uint4 lo, hi;
-        frag_codes(tb, wn * WN + ni * 16 + (lane & 15), ch, lo, hi);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = wn * WN + nt * 16 + rr;
+        const uint4 lo = lds16(tb, col, 2 * g), hi = lds16(tb, col, 2 * g + 1);
         const v8i fb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const float sbc = (SB_MODE == SB_ROWS) ? lsb[col] : 1.0f;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[mi], fb, v4f{0.f, 0.f, 0.f, 0.f},
+        for (int mt = 0; mt < MT; ++mt) {
+          // E4M3 x E4M3 (format selectors 0, 0), no block scaling in the MFMA.
+          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[mt], fb, v4f{0.f, 0.f, 0.f, 0.f},
                                                                          0, 0, 0, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float s = (SB_MODE == SB_BLOCK) ? sa[mi][r] : sa[mi][r] * sb[ni];
-            acc[mi][ni][r] = fmaf(p[r], s, acc[mi][ni][r]);
+          for (int e = 0; e < 4; ++e) {
+            const float sc = (SB_MODE == SB_ROWS) ? s[mt][e] * sbc : s[mt][e];
+            acc[mt][nt][e] = fmaf(p[e], sc, acc[mt][nt][e]);
           }
         }
-        // Keep at most one column of partials live (register budget).
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      v8h fa[MI][4];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        uint4 lo, hi;
-        frag_codes(ta, wm * WM + mi * 16 + (lane & 15), ch, lo, hi);
-        cvt_frag(lo, hi, fa[mi]);
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        uint4 lo, hi;
-        frag_codes(tb, wn * WN + ni * 16 + (lane & 15), ch, lo, hi);
-        v8h fb[4];
-        cvt_frag(lo, hi, fb);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          v4f p = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) p = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[mi][c], fb[c], p, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float s = (SB_MODE == SB_BLOCK) ? sa[mi][r] : sa[mi][r] * sb[ni];
-            acc[mi][ni][r] = fmaf(p[r], s, acc[mi][ni][r]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (NS == 3 && fill)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));   // block lb+1 landed, lb+2 may fly
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();                  // everyone's fill landed; `cur` may be refilled
+  };
 
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's staging of block lb+1 has landed
-    __syncthreads();                  // ... and everyone's; block lb is no longer read
+  stage_all(0, lds0);
+  if (NS == 3 && nLB > 1) {
+    stage_all(1, lds1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  __syncthreads();
+  if (NS == 2) {
+    for (int lb = 0; lb < nLB; lb += 2) {
+      step(lds0, lds1, lb);
+      if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
+    }
+  } else {
+    for (int lb = 0; lb < nLB; lb += 3) {
+      step(lds0, lds2, lb);
+      if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
+      if (lb + 2 < nLB) step(lds2, lds1, lb + 2);
+    }
   }
 
-  // Epilogue: lane owns rows rbase + 16 mi + r, columns cbase + 16 ni.
+  // Epilogue.  Row of accumulator e in sub-tile mt, column of sub-tile nt.
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = rbase + mi * 16 + r;
+    for (int e = 0; e < ACC; ++e) {
+      const int rloc = (PREC == PREC_F16) ? 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) : 4 * (lane >> 4) + e;
+      const int64_t row = i0 + wm * WM + mt * T + rloc;
       if (row >= I) continue;
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int64_t col = cbase + ni * 16;
-        const float v = acc[mi][ni][r];
+      for (int nt = 0; nt < NT; ++nt) {
+        const int64_t col = j0 + wn * WN + nt * T + (lane & (T - 1));
+        const float v = acc[mt][nt][e];
         if (OUT == OUT_F32) {
           static_cast<float*>(Cout)[row * ldc + col] = v;
         } else if (OUT == OUT_F32_ACC) {
@@ -306,20 +385,29 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void* __restrict__ C, in
   }
 }
 
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC>
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS>
 void launch_cfg(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                 const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
                 int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
   const int tilesM = (int)((I + BM - 1) / BM), tilesN = (int)(J / BN);
-  hipLaunchKernelGGL((block_gemm_kernel<BM, BN, WM, WN, SB_MODE, OUT, PREC>), dim3(tilesM * tilesN),
-                     dim3(kThreads), 0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+  hipLaunchKernelGGL((block_gemm_kernel<BM, BN, WM, WN, SB_MODE, OUT, PREC, NW, NS>), dim3(tilesM * tilesN),
+                     dim3(64 * NW), 0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
 }
 
+constexpr int kCUs = 256;   // MI355X compute units
+
+// Tile choice: 256 x 128 output tiles (8 waves of 64 x 64, triple-buffered
+// LDS, one workgroup per CU) when they still give every CU a tile; otherwise
+// 128 x 128 tiles (4 waves, double-buffered, two workgroups per CU).
 template <int SB_MODE, int OUT, int PREC>
 void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                  const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
                  int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
-  launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
+  const int64_t big_tiles = ((I + 255) / 256) * (J / 128);
+  if (big_tiles >= kCUs)
+    launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
+  else
+    launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC, 4, 2>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
 }
 
 }  // namespace

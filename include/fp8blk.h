@@ -58,7 +58,7 @@ extern "C" {
 typedef enum fp8blk_status {
   FP8BLK_OK = 0,
   FP8BLK_INVALID_ARG = 1,        /* null pointer, negative size, ld too small, bad enum */
-  FP8BLK_UNSUPPORTED_SHAPE = 2,  /* GEMM: N or K not a multiple of 128 */
+  FP8BLK_UNSUPPORTED_SHAPE = 2,  /* GEMM: N or K not a multiple of 128, or an operand of 2 GiB or more */
   FP8BLK_MISALIGNED = 3,         /* pointer or leading dimension alignment */
   FP8BLK_WORKSPACE_TOO_SMALL = 4,
   FP8BLK_DEVICE_UNSUPPORTED = 5, /* current device is not gfx950 */
