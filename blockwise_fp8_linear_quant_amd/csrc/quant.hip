@@ -8,8 +8,9 @@
 //
 // Every kernel reads BF16 once with 16-byte loads, reduces the group maximum
 // exactly (max of |x| in binary32), forms s = fl32(amax / 448) and writes
-// E4M3(fl32(x / s)) with the exact quotient of fp8_codec.h.  Zero groups get
-// s = 0 and codes 0x00.
+// E4M3(fl32(x / s)) with the exact quotient of fp8_codec.h and the hardware
+// round-to-nearest-even conversion (see enc4).  Zero groups get s = 0 and
+// codes 0x00.
 #include "internal.h"
 #include "fp8_codec.h"
 
@@ -52,12 +53,42 @@ __device__ __forceinline__ float elem(const uint4& v, int i) {
   return (i & 1) ? bits_f32(w & 0xffff0000u) : bits_f32(w << 16);
 }
 
-__device__ __forceinline__ uint32_t code_of(float x, const GroupQ& g) {
-  return e4m3_encode(group_quotient(x, g)) & 0xffu;
+// Hardware E4M3 conversion.  v_cvt_pk_fp8_f32 rounds to nearest even with
+// subnormals and signed zeros exactly like the format definition for every
+// |v| < 464 (checked exhaustively against the software encoder on gfx950);
+// at 464 and above it returns NaN instead of saturating.  Group quotients are
+// at most ~449.5 in magnitude (|x| <= amax and s = fl32(amax / 448), even for
+// denormal s), so the quantisers use it directly.
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);   // bytes 0, 1
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);  // bytes 2, 3
 }
 
-__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return a | (b << 8) | (c << 16) | (d << 24);
+// Codes of four values of one group, packed little-endian into a dword.
+__device__ __forceinline__ uint32_t code4(float a, float b, float c, float d, const GroupQ& g) {
+  return enc4(group_quotient(a, g), group_quotient(b, g), group_quotient(c, g), group_quotient(d, g));
+}
+
+// Any binary32 -> E4M3 code: hardware below 464, saturation at and above it
+// (infinities included); NaN keeps the hardware's NaN code.
+__device__ __forceinline__ uint32_t encode_any(float x) {
+  const uint32_t u = f32_bits(x), a = u & 0x7fffffffu;
+  uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xffu;
+  if (a >= 0x43e80000u && a <= 0x7f800000u) c = 0x7eu | ((u >> 24) & 0x80u);
+  return c;
+}
+
+// 4x4 byte transpose: rows r[0..3] (byte j = column j) -> columns c[0..3]
+// (byte i = row i).  v_perm_b32 picks bytes of (S0 << 32 | S1).
+__device__ __forceinline__ void transpose4x4(const uint32_t (&r)[4], uint32_t (&c)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
+  const uint32_t t1 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
+  const uint32_t t2 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+  c[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  c[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  c[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  c[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
 // Store 8 code bytes at p[0..7], only columns col+i < C.
@@ -107,9 +138,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;   // zero group -> codes 0x00
   uint32_t w[4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
-    w[d] = keep & pack4(code_of(f[4 * d], gq), code_of(f[4 * d + 1], gq),
-                        code_of(f[4 * d + 2], gq), code_of(f[4 * d + 3], gq));
+  for (int d = 0; d < 4; ++d) w[d] = keep & code4(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], gq);
   if (row_ok) {
     uint8_t* qr = q + row * ldq;
     if (col0 < C) store8(qr + col0, col0, C, w[0], w[1]);
@@ -160,8 +189,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
     uint32_t w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
-      w[d] = keep & pack4(code_of(elem(v[4 * d], j), gq), code_of(elem(v[4 * d + 1], j), gq),
-                          code_of(elem(v[4 * d + 2], j), gq), code_of(elem(v[4 * d + 3], j), gq));
+      w[d] = keep & code4(elem(v[4 * d], j), elem(v[4 * d + 1], j), elem(v[4 * d + 2], j), elem(v[4 * d + 3], j), gq);
     if (f0 + j < C) {
       *reinterpret_cast<uint4*>(qT + (f0 + j) * ldq + t0) = make_uint4(w[0], w[1], w[2], w[3]);
       if (b == 0) s[tg * lds + f0 + j] = gq.s;
@@ -206,25 +234,33 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
 
   const GroupQ gq = group_setup(m);
   const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
-  uint32_t cd[8][8];
+  // Row-major codes: rw[i][0] = columns 0..3 of row i, rw[i][1] = columns 4..7.
+  uint32_t rw[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cd[i][j] = code_of(elem(v[i], j), gq);
-
+    for (int hh = 0; hh < 2; ++hh)
+      rw[i][hh] = keep & code4(elem(v[i], 4 * hh), elem(v[i], 4 * hh + 1), elem(v[i], 4 * hh + 2),
+                               elem(v[i], 4 * hh + 3), gq);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (r0 + i < R && c0 < C)
-      store8(q + (r0 + i) * ldq + c0, c0, C, keep & pack4(cd[i][0], cd[i][1], cd[i][2], cd[i][3]),
-             keep & pack4(cd[i][4], cd[i][5], cd[i][6], cd[i][7]));
-  }
+  for (int i = 0; i < 8; ++i)
+    if (r0 + i < R && c0 < C) store8(q + (r0 + i) * ldq + c0, c0, C, rw[i][0], rw[i][1]);
   if (qT != nullptr) {
+    // Transposed copy: column j of this thread's 8x8 block = rows 0..7 of it.
+    uint32_t cw[8][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (c0 + j < C && r0 < R)
-        store8(qT + (c0 + j) * ldqT + r0, r0, R, keep & pack4(cd[0][j], cd[1][j], cd[2][j], cd[3][j]),
-               keep & pack4(cd[4][j], cd[5][j], cd[6][j], cd[7][j]));
-    }
+    for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t rr[4] = {rw[4 * rb2][hh], rw[4 * rb2 + 1][hh], rw[4 * rb2 + 2][hh], rw[4 * rb2 + 3][hh]};
+        uint32_t cc[4];
+        transpose4x4(rr, cc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cw[4 * hh + j][rb2] = cc[j];
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < C && r0 < R) store8(qT + (c0 + j) * ldqT + r0, r0, R, cw[j][0], cw[j][1]);
   }
   if (t == 0) {
     const int64_t nbr = (R + 127) / 128, nbc = (C + 127) / 128;
@@ -235,7 +271,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
 
 __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x, uint8_t* __restrict__ q, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) q[i] = (uint8_t)e4m3_encode(x[i]);
+  if (i < n) q[i] = (uint8_t)encode_any(x[i]);
 }
 
 }  // namespace

@@ -1,5 +1,7 @@
 """GPU parity of the device E4M3 encoder (through fp8_e4m3_encode) against the
-oracle, on every positive binary32 in [2^-12, 2^10) and on random bit patterns."""
+oracle, on every binary32 of magnitude in [2^-12, 2^10) (both signs) and on
+random bit patterns.  The encoder shares the hardware conversion the
+quantisers use, so this also pins that conversion."""
 
 import numpy as np
 import pytest
@@ -22,8 +24,8 @@ def test_device_encoder_exhaustive_decision_range():
         got = B.fp8_e4m3_encode(torch.from_numpy(v).cuda()).cpu().numpy()
         ref = e4m3.encode(v)
         assert np.array_equal(got, ref), hex(start)
-        neg = B.fp8_e4m3_encode(torch.from_numpy(-v[::97]).cuda()).cpu().numpy()
-        assert np.array_equal(neg, ref[::97] | 0x80)
+        neg = B.fp8_e4m3_encode(torch.from_numpy(-v).cuda()).cpu().numpy()
+        assert np.array_equal(neg, ref | 0x80), hex(start)
 
 
 def test_device_encoder_random_and_specials():
