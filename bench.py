@@ -30,6 +30,9 @@ sys.path.insert(0, ROOT)
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
+# HBM bytes per block-GEMM launch from FETCH_SIZE/WRITE_SIZE counters of this
+# workload (used only while the summary's kernel-source digest still matches).
+TRAFFIC_SUMMARY = "block_gemm_traffic_layer_m4096.txt"
 
 
 def parse():
@@ -41,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--no-fp8-path", action="store_true", help="skip timing the FP8 matrix-core GEMM path")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="launch one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
 
 
@@ -69,6 +74,19 @@ class LayerBuffers:
     def flops(self):
         return 3 * 2 * self.M * self.n * self.k
 
+    def gemm_flops(self):
+        """2*M*N*K of the fwd, dgrad and wgrad GEMMs (all three equal)."""
+        return [2 * self.M * self.n * self.k] * 3
+
+    def gemm_bytes(self):
+        """Algorithmic bytes of the fwd, dgrad and wgrad GEMMs: operands once, scales, output."""
+        M, n, k = self.M, self.n, self.k
+        mp = -(-M // 128) * 128
+        fwd = M * k + n * k + 4 * M * (k // 128) + 4 * (n // 128) * (k // 128) + 2 * M * n
+        dgrad = M * n + k * n + 4 * M * (n // 128) + 4 * (k // 128) * (n // 128) + 2 * M * k
+        wgrad = n * mp + k * mp + 4 * (n + k) * (mp // 128) + 4 * n * k
+        return [fwd, dgrad, wgrad]
+
     def quant_bytes(self):
         M, n, k = self.M, self.n, self.k
         row = lambda r, c: r * c * 3 + r * (-(-c // 128)) * 4          # 2 B in, 1 B out, scales
@@ -83,11 +101,17 @@ class LayerBuffers:
         B.fp8_quant_1x128(self.dy, q=self.dyq, scales=self.sdy)
         B.fp8_quant_1x128(self.dy, transpose_out=True, q=self.dyqT, scales=self.sdyT)
 
-    def gemms(self, B, fp8_mc=False):
+    def gemms(self, B, fp8_mc=False, ev=None):
+        """The three GEMMs; `ev` (4 events) brackets each launch when given."""
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
         B.fp8_block_gemm_fwd(self.xq, self.sx, self.wq, self.sw, y=self.y, fp8_matrix_core=fp8_mc)
+        rec(1)
         B.fp8_block_gemm_dgrad(self.dyq, self.sdy, self.wqT, self.swT, dx=self.dx, fp8_matrix_core=fp8_mc)
+        rec(2)
         B.fp8_block_gemm_wgrad(self.dyqT, self.sdyT, self.xqT, self.sxT, M=self.M, dw=self.dw,
                                fp8_matrix_core=fp8_mc)
+        rec(3)
 
 
 def cpu_baseline(W, layers, sample_tokens):
@@ -120,6 +144,19 @@ def cpu_baseline(W, layers, sample_tokens):
                       f"tokens, numpy float64 oracle, {dt:.1f} s"}
 
 
+def copy_probe(torch, dev, mib):
+    """A plain device copy of known size (float32 multiply by one), launched once.
+
+    Under ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` its counters give the
+    bytes-per-unit factor that turns the GEMM's counters into HBM bytes."""
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return n * 4
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -128,31 +165,30 @@ def main():
         sys.exit(2)
     import torch
     from blockwise_fp8_linear_quant_amd import binding as B
+    from blockwise_fp8_linear_quant_amd import profiling
     from blockwise_fp8_linear_quant_amd import workloads as W
 
     dev = torch.device("cuda:0")
     M = args.tokens
     layers = [LayerBuffers(torch, B, W, n, k, nout, M, dev) for n, k, nout in W.LINEARS]
     torch.cuda.synchronize()
+    if args.copy_probe_mib:
+        copy_probe(torch, dev, args.copy_probe_mib)
 
     def step(evs=None, fp8_mc=False):
         for i, L in enumerate(layers):
             if evs is not None:
                 evs[i][0].record()
             L.quantise(B)
-            if evs is not None:
-                evs[i][1].record()
-            L.gemms(B, fp8_mc)
-            if evs is not None:
-                evs[i][2].record()
+            L.gemms(B, fp8_mc, evs[i][1:] if evs is not None else None)
 
     def timed(fp8_mc):
-        """K timed steps; returns (ms/step, GEMM ms/step, quantiser ms/step, wall s)."""
+        """K timed steps -> (ms/step, per-GEMM ms [linear][op], quantiser ms/step, wall s)."""
         for _ in range(args.warmup):
             step(fp8_mc=fp8_mc)
         torch.cuda.synchronize()
         mk = lambda: torch.cuda.Event(enable_timing=True)
-        evs = [[(mk(), mk(), mk()) for _ in layers] for _ in range(args.steps)]
+        evs = [[[mk() for _ in range(5)] for _ in layers] for _ in range(args.steps)]
         start, end = mk(), mk()
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
@@ -163,23 +199,39 @@ def main():
         torch.cuda.synchronize()
         t_wall = time.perf_counter() - t_wall
         ms_step = start.elapsed_time(end) / args.steps
-        gemm_ms = sum(b.elapsed_time(c) for row in evs for (a, b, c) in row) / args.steps
-        quant_ms = sum(a.elapsed_time(b) for row in evs for (a, b, c) in row) / args.steps
-        return ms_step, gemm_ms, quant_ms, t_wall
+        per_gemm = [[sum(evs[s][i][o + 1].elapsed_time(evs[s][i][o + 2]) for s in range(args.steps)) / args.steps
+                     for o in range(3)] for i in range(len(layers))]
+        quant_ms = sum(evs[s][i][0].elapsed_time(evs[s][i][1])
+                       for s in range(args.steps) for i in range(len(layers))) / args.steps
+        return ms_step, per_gemm, quant_ms, t_wall
 
     # Timed region (default path: exact block products on the F16 matrix path).
-    ms_step, gemm_ms, quant_ms, t_wall = timed(False)
+    ms_step, per_gemm, quant_ms, t_wall = timed(False)
     flops = sum(L.flops() for L in layers)
+    gemm_ms = sum(sum(r) for r in per_gemm)
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["f16"]
+    n_launch = 3 * len(layers)
+    alg_bytes = sum(sum(L.gemm_bytes()) for L in layers) / n_launch
+    gemms = {}
+    for L, row in zip(layers, per_gemm):
+        for op, ms, fl in zip(("fwd", "dgrad", "wgrad"), row, L.gemm_flops()):
+            gemms[f"{op}_{L.name}"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
     qbytes = sum(L.quant_bytes() for L in layers)
+
+    traffic = None
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY))
+    if tr is not None and args.tokens == 4096:
+        traffic = float(tr["gemm_hbm_bytes_per_launch"])
+
     fast = None
     if not args.no_fp8_path:
         f_ms, f_gemm, f_q, _ = timed(True)
+        f_gemm_ms = sum(sum(r) for r in f_gemm)
         fast = {"ms_per_step": round(f_ms, 4), "value": round(flops / (f_ms * 1e-3) / 1e12, 3),
-                "gemm_tflops": round(flops / (f_gemm * 1e-3) / 1e12, 3),
-                "gemm_frac_of_fp8_peak": round(flops / (f_gemm * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                "gemm_tflops": round(flops / (f_gemm_ms * 1e-3) / 1e12, 3),
+                "gemm_frac_of_fp8_peak": round(flops / (f_gemm_ms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                 "note": "fp8_block_gemm with FP8BLK_GEMM_FP8_MATRIX_CORE: v_mfma_f32_16x16x128_f8f6f4 block "
                         "products, hardware-truncated inside groups of 8 (not the default path)"}
 
@@ -200,10 +252,15 @@ def main():
                                f"gate_up 2048->12288, down 6144->2048), quantise + fwd + dgrad + wgrad",
                    "tokens": M, "hidden": 2048, "intermediate": 6144, "gemm_gflop_per_step": round(flops / 1e9, 3)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / peak, 4), "traffic": None,
+                     "frac": round(gemm_tflops / peak, 4),
+                     "traffic": round(traffic) if traffic is not None else None,
+                     "algorithmic_bytes_per_launch": round(alg_bytes),
                      "kernel": "block_gemm_kernel (E4M3 codes -> exact F16 MFMA, FP32 block rescale)",
+                     "launches_per_step": n_launch,
+                     "avg_launch_us": round(gemm_ms / n_launch * 1e3, 2),
                      "gemm_ms_per_step": round(gemm_ms, 4),
                      "frac_of_fp8_peak": round(gemm_tflops / PEAK_TFLOPS["fp8"], 4)},
+        "gemms": gemms,
         "quantisers": {"ms_per_step": round(quant_ms, 4), "algorithmic_gb": round(qbytes / 1e9, 4),
                        "gbps": round(qbytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms > 0 else None,
                        "frac_hbm_peak": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)

@@ -1,0 +1,173 @@
+"""Summaries of rocprofv3 output for the committed profile notes.
+
+Two kinds of summary are written as short text files:
+
+* ``stats``: the per-kernel table of a ``rocprofv3 --kernel-trace --stats
+  --output-format csv`` run (calls, average and total duration, share).
+* ``traffic``: HBM bytes per dispatch of the block GEMM from two
+  ``rocprofv3 --pmc`` runs (``FETCH_SIZE``, then ``WRITE_SIZE``) of the same
+  command.  Both counters are scaled by what they read for a plain device copy
+  of known size launched in the same process (``bench.py --copy-probe-mib``),
+  so the figure is in bytes rather than in the counters' own units.
+
+The traffic summary records a digest of the GEMM kernel's source and build
+flags; ``bench.py`` reports the figure only while that digest still matches,
+so a changed kernel never carries counters taken from an older one.
+
+Usage (on the CPU, after the profiler runs):
+  python -m blockwise_fp8_linear_quant_amd.profiling stats KERNEL_STATS.csv OUT.txt --command "..."
+  python -m blockwise_fp8_linear_quant_amd.profiling traffic FETCH.csv WRITE.csv OUT.txt \
+      --copy-bytes N --command "..."
+"""
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/internal.h", "build.py")
+GEMM_KERNEL = "block_gemm_kernel"
+COPY_KERNEL_HINTS = ("copy", "elementwise")
+
+
+def source_digest(files=GEMM_SOURCES):
+    """sha256 over the GEMM kernel's source files and the build script (its flags)."""
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(_HERE, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def short_name(name):
+    """Kernel name without namespaces and the parameter list; template arguments kept."""
+    name = re.sub(r"^void ", "", name)
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and i > 0 and name[i - 1] != ":":
+            if not name.startswith("(anonymous", i):
+                cut = i
+                break
+    name = name[:cut]
+    return name.replace("fp8blk::(anonymous namespace)::", "")
+
+
+def stats_summary(stats_csv, command, steps=None):
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"command: {command}", "",
+             f"{'kernel':<78} {'calls':>6} {'avg_us':>9} {'total_ms':>9} {'share%':>7}"]
+    for r in rows:
+        lines.append(f"{short_name(r['Name'])[:78]:<78} {int(r['Calls']):>6} "
+                     f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['TotalDurationNs']) / 1e6:>9.3f} "
+                     f"{float(r['Percentage']):>7.2f}")
+    gemm = [r for r in rows if GEMM_KERNEL in r["Name"]]
+    if gemm:
+        calls = sum(int(r["Calls"]) for r in gemm)
+        tot = sum(float(r["TotalDurationNs"]) for r in gemm)
+        lines += ["", f"{GEMM_KERNEL} (all instantiations): {calls} calls, average {tot / calls / 1e3:.2f} us"]
+        if steps:
+            lines.append(f"per step ({steps} steps incl. warmup): {tot / steps / 1e3:.1f} us")
+    return "\n".join(lines) + "\n"
+
+
+def _dispatch_counters(path, counter):
+    """{dispatch id: (kernel name, value)} for one counter of a counter_collection CSV."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, val = r["Kernel_Name"], float(r["Counter_Value"])
+        if d in out:   # one row per agent/XCD instance in some versions: add them
+            out[d] = (name, out[d][1] + val)
+        else:
+            out[d] = (name, val)
+    return out
+
+
+def traffic_summary(fetch_csv, write_csv, copy_bytes, command, algorithmic_bytes_per_launch=None):
+    fetch = _dispatch_counters(fetch_csv, "FETCH_SIZE")
+    write = _dispatch_counters(write_csv, "WRITE_SIZE")
+
+    def copy_value(tab):
+        cands = [(d, v) for d, (n, v) in tab.items()
+                 if GEMM_KERNEL not in n and any(h in n.lower() for h in COPY_KERNEL_HINTS)]
+        if not cands:
+            raise SystemExit("no copy kernel dispatch found in the counter CSV")
+        return max(cands, key=lambda dv: dv[1])[1]   # the big copy of known size
+
+    f_copy_kib, w_copy_kib = copy_value(fetch), copy_value(write)
+    f_scale = copy_bytes / f_copy_kib   # bytes per counter unit
+    w_scale = copy_bytes / w_copy_kib
+    gf = [v for n, v in fetch.values() if GEMM_KERNEL in n]
+    gw = [v for n, v in write.values() if GEMM_KERNEL in n]
+    if not gf or not gw:
+        raise SystemExit("no block GEMM dispatch in the counter CSVs")
+    fetch_b = sum(gf) / len(gf) * f_scale
+    write_b = sum(gw) / len(gw) * w_scale
+    lines = [
+        f"command: {command}",
+        f"source_sha256: {source_digest()}",
+        f"copy_probe_bytes: {copy_bytes}",
+        f"copy_probe_fetch_kib: {f_copy_kib:.1f}",
+        f"copy_probe_write_kib: {w_copy_kib:.1f}",
+        f"fetch_scale_bytes_per_kib: {f_scale:.2f}",
+        f"write_scale_bytes_per_kib: {w_scale:.2f}",
+        f"gemm_dispatches: {len(gf)}",
+        f"gemm_fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"gemm_write_bytes_per_launch: {write_b:.0f}",
+        f"gemm_hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+    ]
+    if algorithmic_bytes_per_launch:
+        lines.append(f"gemm_algorithmic_bytes_per_launch: {algorithmic_bytes_per_launch:.0f}")
+        lines.append(f"traffic_over_algorithmic: {(fetch_b + write_b) / algorithmic_bytes_per_launch:.3f}")
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(path):
+    """The traffic summary as a dict, or None if missing or taken from another kernel source."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    return kv
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("out")
+    s.add_argument("--command", required=True)
+    s.add_argument("--steps", type=int)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("out")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--algorithmic-bytes", type=float)
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        text = stats_summary(a.stats_csv, a.command, a.steps)
+    else:
+        text = traffic_summary(a.fetch_csv, a.write_csv, a.copy_bytes, a.command, a.algorithmic_bytes)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text, end="")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,47 @@
+"""Host checks of the rocprofv3 summary helpers (synthetic CSVs, no GPU)."""
+
+import csv
+
+from blockwise_fp8_linear_quant_amd import profiling
+
+GEMM = ("void fp8blk::(anonymous namespace)::block_gemm_kernel<256, 128, 64, 64, 0, 1, 0, 8, 3>"
+        "(unsigned char const*, long, float const*, long)")
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>(int, float*)"
+
+
+def test_short_name_keeps_template_arguments():
+    assert profiling.short_name(GEMM) == "block_gemm_kernel<256, 128, 64, 64, 0, 1, 0, 8, 3>"
+    q = "fp8blk::(anonymous namespace)::quant_rows_kernel(unsigned short const*, long)"
+    assert profiling.short_name(q) == "quant_rows_kernel"
+
+
+def _counters(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, name, v in rows:
+            w.writerow([d, name, counter, v])
+
+
+def test_traffic_scales_by_the_copy_probe(tmp_path):
+    copy_bytes = 1 << 30
+    # counters read half the true bytes for the copy, so the scale is 2048 B per unit
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counters(fetch, "FETCH_SIZE", [(1, COPY, 524288.0), (2, GEMM, 1000.0), (3, GEMM, 3000.0)])
+    _counters(write, "WRITE_SIZE", [(1, COPY, 1048576.0), (2, GEMM, 10.0), (3, GEMM, 30.0)])
+    text = profiling.traffic_summary(str(fetch), str(write), copy_bytes, "cmd", 4096.0 * 1000)
+    kv = dict(line.split(": ", 1) for line in text.strip().splitlines())
+    assert float(kv["fetch_scale_bytes_per_kib"]) == 2048.0
+    assert float(kv["write_scale_bytes_per_kib"]) == 1024.0
+    assert int(kv["gemm_fetch_bytes_per_launch"]) == 2000 * 2048
+    assert int(kv["gemm_write_bytes_per_launch"]) == 20 * 1024
+    assert kv["source_sha256"] == profiling.source_digest()
+
+
+def test_read_traffic_rejects_another_source(tmp_path):
+    p = tmp_path / "t.txt"
+    p.write_text("source_sha256: 0000\ngemm_hbm_bytes_per_launch: 5\n")
+    assert profiling.read_traffic(str(p)) is None
+    p.write_text(f"source_sha256: {profiling.source_digest()}\ngemm_hbm_bytes_per_launch: 5\n")
+    assert profiling.read_traffic(str(p))["gemm_hbm_bytes_per_launch"] == "5"
+    assert profiling.read_traffic(str(tmp_path / "missing.txt")) is None
