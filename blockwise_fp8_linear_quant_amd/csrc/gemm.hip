@@ -16,26 +16,27 @@
 //     wgrad    C = dW [N, K]: A = dYqT [N, M],  B = XqT [K, M]   (SB per row)
 //
 // gfx950 design:
-//   * operands stay E4M3 in HBM and LDS (one byte per element); each
+//   * operands stay E4M3 in HBM and LDS (one byte per element).  Each
 //     workgroup stages a BM x 128 tile of A, a BN x 128 tile of B and their
-//     per-row scales per scale block with global_load_lds (no VGPR round
-//     trip) into one of several LDS buffers, so block lb+1 streams in while block
-//     lb is multiplied (large problems: three buffers, block lb+2 in flight).
-//     The buffers are distinct LDS objects and the block loop is unrolled by
-//     the buffer count, which lets the compiler see that reads of one buffer
-//     never wait for the fill of another.  Rows are 128 bytes with
-//     the 16-byte chunks XOR-swizzled by (row % 8), so fragment reads
-//     (ds_read_b128) are bank-conflict free;
+//     per-row scales per scale block straight into LDS (global_load_lds, no
+//     VGPR round trip), into one of several buffers: for large problems three,
+//     so blocks lb+1 and lb+2 stream in while block lb is multiplied.  The
+//     buffers are distinct LDS objects and the block loop is unrolled by the
+//     buffer count.  Fills are waited for explicitly and synchronised with an
+//     LDS-only barrier (a full __syncthreads() would drain every fill in
+//     flight).  Rows are 128 bytes with the 16-byte chunks XOR-swizzled by
+//     (row / 2) % 8, so fragment reads (ds_read_b128) are bank-conflict free;
 //   * the block product of a sub-tile is formed in the matrix core from a zero
 //     accumulator and folded into FP32 register accumulators with one FMA per
 //     element and block (acc = fma(P_lb, SA*SB, acc)):
-//       PREC_F16 (default, exact): E4M3 codes are converted exactly to F16 in
+//       exact path (default): E4M3 codes are converted exactly to F16 in
 //         registers and multiplied with v_mfma_f32_32x32x16_f16, eight per
-//         32x32 sub-tile and block (the 32x32 shape sustains ~2.1 PF on
-//         MI355X, the 16x16x32 shape about half of that);
-//       PREC_FP8: one v_mfma_f32_16x16x128_f8f6f4 per 16x16 sub-tile and
-//         block (twice the matrix rate, but the hardware truncates small
-//         products inside groups of 8, see Prec);
+//         32x32 sub-tile and block; the K slices of a block are read from LDS
+//         one ahead of the multiply, and the first slice of the next block is
+//         read while the last one is multiplied;
+//       FP8 matrix-core path (opt-in): one v_mfma_f32_16x16x128_f8f6f4 per
+//         16x16 sub-tile and block (twice the matrix rate, but the hardware
+//         truncates small products inside groups of 8, see Prec);
 //   * workgroups are renumbered so that each of the 8 XCDs (own L2) works on a
 //     contiguous range of output tiles, grouped 8 tile-rows at a time.
 #include "internal.h"
@@ -60,6 +61,10 @@ constexpr int kGroupM = 8;
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained; gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
+// The same with an lgkmcnt limit as well (63 leaves vmcnt unconstrained).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | (0x7 << 4) | ((lgkm & 0xF) << 8) | (((vm >> 4) & 3) << 14);
+}
 
 // PREC selects how the 128-term block product is formed:
 //   PREC_F16: the E4M3 codes are converted exactly to F16 in registers
@@ -99,17 +104,57 @@ __device__ __forceinline__ void map_tile(int pid, int nblocks, int tilesM, int t
   tn = in_group / gm;
 }
 
-// Byte offset of 16-byte chunk `chunk` of tile row `row` in LDS.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// releases global memory, which makes every wave wait for all of its
+// outstanding global loads (vmcnt(0)) -- including the direct-to-LDS fills of
+// blocks that are meant to stay in flight across the barrier.  Fills that must
+// have landed are waited for explicitly (s_waitcnt vmcnt) before this call.
+// The wave's own LDS reads are completed first (lgkmcnt(0)), so no fill
+// issued after the barrier can overwrite data a read has not fetched yet; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Byte offset of 16-byte chunk `chunk` of tile row `row` in LDS.  gfx950
+// serves a ds_read_b128 sixteen lanes at a time from 256 bytes of banks, so
+// the sixteen rows a fragment read touches must land in sixteen distinct
+// 16-byte bank slots: row parity picks the 128-byte half, and the chunk is
+// XOR-ed with (row / 2) % 8 (measured conflict-free; XOR with row % 8 makes
+// rows r and r + 8 collide, 4 extra cycles per read).
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key(row)) << 4); }
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* tile, int row, int chunk) {
   return *reinterpret_cast<const uint4*>(tile + swz(row, chunk));
 }
 
+// Direct-to-LDS copies (global_load_lds, saddr form): lane L copies 16 (or 4)
+// bytes from base + voff to LDS address lds + 16 L (4 L).  They are issued from
+// inline assembly on purpose: for the builtin, the compiler cannot tell which
+// LDS buffer a fill targets and makes every later LDS read wait for all fills
+// in flight (vmcnt(0)), which would serialise the multi-buffered pipeline.  The
+// statements have no register outputs; every consumer of a fill waits for it
+// explicitly (s_waitcnt vmcnt) and then synchronises the workgroup.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t)p;
+}
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
+               :: "s"(base), "v"(voff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, %0"
+               :: "s"(base), "v"(voff), "s"(lds) : "memory", "m0");
+}
+
 // Direct-to-LDS staging.  A tile of ROWS rows x 128 bytes moves with ROWS/8
 // wave instructions of 1 KB; lane L of instruction `blk` writes LDS bytes
-// [16L, 16L+16) of its 1 KB, i.e. tile row 8 blk + L/8, slot L%8, which must
-// hold global chunk (L%8) ^ (L/8) of that row.  The per-lane byte offsets of
+// [16L, 16L+16) of its 1 KB, i.e. tile row r = 8 blk + L/8, slot L%8, which
+// must hold global chunk (L%8) ^ swz_key(r) of that row.  The per-lane byte offsets of
 // the source rows are loop invariant (computed once, 32-bit: every operand
 // here is below 2 GiB); per scale block only the wave-uniform base pointer
 // moves, so each load is one instruction with no address arithmetic.  Rows
@@ -123,16 +168,17 @@ struct TileStager {
   __device__ __forceinline__ void init(int64_t ld, int64_t r0, int64_t rmax, int wave, int lane) {
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
-      int64_t row = r0 + 8 * (NW * u + wave) + (lane >> 3);
+      const int trow = 8 * (NW * u + wave) + (lane >> 3);   // row within the tile
+      int64_t row = r0 + trow;
       row = row < rmax ? row : rmax;
-      off[u] = (uint32_t)(row * ld) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+      off[u] = (uint32_t)(row * ld) + (uint32_t)(((lane & 7) ^ swz_key(trow)) * 16);
     }
   }
   // base: G + lb * 128 (wave-uniform); dst: the tile in LDS.
   __device__ __forceinline__ void issue(const uint8_t* base, uint8_t* dst, int wave) const {
+    const uint32_t l0 = lds_addr(dst) + wave * 1024;
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u)
-      __builtin_amdgcn_global_load_lds((gbl_void_t)(base + off[u]), (lds_void_t)(dst + (NW * u + wave) * 1024), 16, 0, 0);
+    for (int u = 0; u < kLoads; ++u) dma_b128(base, off[u], l0 + NW * u * 1024);
   }
 };
 
@@ -150,9 +196,8 @@ struct ScaleStager {
   }
   // base: SC + lb * ld (wave-uniform).
   __device__ __forceinline__ void issue(const float* base, float* dst, int wave, int lane) const {
-    if (lane < kPerWave)
-      __builtin_amdgcn_global_load_lds((gbl_void_t)(reinterpret_cast<const uint8_t*>(base) + off),
-                                       (lds_void_t)(dst + kPerWave * wave), 4, 0, 0);
+    const uint32_t l0 = lds_addr(dst + kPerWave * wave);
+    if (lane < kPerWave) dma_b32(base, off, l0);
   }
 };
 
@@ -174,12 +219,212 @@ struct Cfg {
   static constexpr int kBufBytes = kSbOff + (SB_MODE == SB_ROWS ? BN * 4 : 0);
 };
 
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS>
-__global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_kernel(
+// Exact path: E4M3 -> F16 in registers, v_mfma_f32_32x32x16_f16; one
+// workgroup per output tile.
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_f16_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
     int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
-  using C = Cfg<BM, BN, WM, WN, SB_MODE, PREC, NW, NS>;
+  using C = Cfg<BM, BN, WM, WN, SB_MODE, PREC_F16, NW, NS>;
+  constexpr int MT = C::MT, NT = C::NT;
+  // One distinct LDS object per pipeline stage (see the file comment).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[NS == 3 ? C::kBufBytes : 16];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  int tm, tn;
+  map_tile(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int nLB = (int)(L / BK);
+  // Lane l: row (l % 32) of a 32x32 sub-tile; half h = l / 32 holds K bytes
+  // [64h, 64h + 64) of the block.  K slice c (0..3) is the 16 bytes at
+  // 64h + 16c, one LDS read per fragment row; MFMA k (0, 1) of the slice takes
+  // its 8 codes at 64h + 16c + 8k.  The MFMA is given the B fragment first, so
+  // it produces the transposed sub-tile: lane l holds output row (l % 32) --
+  // one A row, hence one A scale per lane -- and accumulator 4q + u holds
+  // output column 8q + 4h + u.
+  const int h = lane >> 5, rr = lane & 31;
+
+  float acc[MT][NT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
+
+  TileStager<BM, NW> sta;
+  TileStager<BN, NW> stb;
+  ScaleStager<BM, NW> ssa;
+  ScaleStager<BN, NW> ssb;
+  sta.init(lda, i0, I - 1, wave, lane);
+  stb.init(ldb, j0, j0 + BN - 1, wave, lane);
+  ssa.init(i0, I - 1, wave, lane);
+  ssb.init(j0, j0 + BN - 1, wave, lane);
+  auto stage_all = [&](int lb, uint8_t* buf) {
+    sta.issue(A + (int64_t)lb * BK, buf, wave);
+    stb.issue(B + (int64_t)lb * BK, buf + BM * BK, wave);
+    ssa.issue(SA + (int64_t)lb * ldsa, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
+    if (SB_MODE == SB_ROWS) ssb.issue(SB + (int64_t)lb * ldsb, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
+  };
+
+  uint4 qa[2][MT], qb[2][NT];   // raw codes of two K slices (software pipeline)
+  v8h fa[MT][2], fb[NT][2];     // converted operands of the slice being multiplied
+  v16f p[MT][NT];               // block products
+  auto load_slice = [&](const uint8_t* buf, int c, int slot) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) qa[slot][mt] = lds16(buf, wm * WM + mt * 32 + rr, 4 * h + c);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) qb[slot][nt] = lds16(buf + BM * BK, wn * WN + nt * 32 + rr, 4 * h + c);
+  };
+  auto convert = [&](int slot) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      fa[mt][0] = cvt8(qa[slot][mt].x, qa[slot][mt].y);
+      fa[mt][1] = cvt8(qa[slot][mt].z, qa[slot][mt].w);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      fb[nt][0] = cvt8(qb[slot][nt].x, qb[slot][nt].y);
+      fb[nt][1] = cvt8(qb[slot][nt].z, qb[slot][nt].w);
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          p[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[nt][k], fa[mt][k], p[mt][nt], 0, 0, 0);
+  };
+
+  // Block lb from `cur` (its slice 0 already in registers).  Slices 1..3 are
+  // read one ahead of the multiply.  Once the last slice is in registers the
+  // wave waits for its share of block lb + 1, the workgroup synchronises,
+  // `cur` is refilled with block lb + NS and slice 0 of block lb + 1 is read
+  // from `nxt` -- all while the last slice is multiplied.  The block's scales
+  // are read into registers before `cur` can be refilled.
+  auto step = [&](uint8_t* cur, const uint8_t* nxt, int lb) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) p[mt][nt] = v16f{};
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      load_slice(cur, c + 1, (c + 1) & 1);
+      convert(c & 1);
+      multiply();
+    }
+    convert(1);
+    const float* lsa = reinterpret_cast<const float*>(cur + C::kSaOff);
+    const float* lsb = reinterpret_cast<const float*>(cur + C::kSbOff);
+    float sa[MT];                  // A scale of this lane's output row
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sa[mt] = lsa[wm * WM + mt * 32 + rr];
+    float4 sbr[NT][4];             // SB_ROWS: B scales of output columns 8q + 4h + u
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sbr[nt][q] = (SB_MODE == SB_ROWS) ? *reinterpret_cast<const float4*>(lsb + wn * WN + nt * 32 + 8 * q + 4 * h)
+                                          : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLB + lb] : 1.0f;
+    if (NS == 3 && lb + 2 < nLB)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));   // block lb+1 landed, lb+2 may fly
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    if (lb + NS < nLB) stage_all(lb + NS, cur);
+    if (lb + 1 < nLB) load_slice(nxt, 0, 0);
+    multiply();
+    // Rescale-accumulate: acc += P * SA(row) * SB.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float srow = (SB_MODE == SB_BLOCK) ? sa[mt] * sblk : sa[mt];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float cs[4] = {sbr[nt][q].x, sbr[nt][q].y, sbr[nt][q].z, sbr[nt][q].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float sc = (SB_MODE == SB_ROWS) ? srow * cs[u] : srow;
+            acc[mt][nt][4 * q + u] = fmaf(p[mt][nt][4 * q + u], sc, acc[mt][nt][4 * q + u]);
+          }
+        }
+    }
+  };
+
+  // Prologue: fill every buffer, wait for block 0, read its slice 0.
+  const int pre = nLB < NS ? nLB : NS;
+  stage_all(0, lds0);
+  if (pre > 1) stage_all(1, lds1);
+  if (NS == 3 && pre > 2) stage_all(2, lds2);
+  if (NS == 3 && pre > 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::kVmemPerBlock));
+  else if (pre > 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  load_slice(lds0, 0, 0);
+  if (NS == 2) {
+    for (int lb = 0; lb < nLB; lb += 2) {
+      step(lds0, lds1, lb);
+      if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
+    }
+  } else {
+    for (int lb = 0; lb < nLB; lb += 3) {
+      step(lds0, lds1, lb);
+      if (lb + 1 < nLB) step(lds1, lds2, lb + 1);
+      if (lb + 2 < nLB) step(lds2, lds0, lb + 2);
+    }
+  }
+
+  // Epilogue.  Lane l holds row (l % 32) of each sub-tile and, in
+  // accumulators 4q..4q+3, the four consecutive columns 8q + 4h .. 8q + 4h + 3:
+  // one 8-byte (BF16) or 16-byte (FP32) store each.  The ABI guarantees
+  // 16-byte aligned C with ldc a multiple of 8 (BF16) or 4 (FP32), so these
+  // stores are aligned.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t row = i0 + wm * WM + mt * 32 + rr;
+    if (row >= I) continue;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = j0 + wn * WN + nt * 32 + 8 * q + 4 * h;
+        const float* v = &acc[mt][nt][4 * q];
+        if (OUT == OUT_BF16) {
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + row * ldc + col) = make_uint2(lo, hi);
+        } else {
+          float4* dst = reinterpret_cast<float4*>(static_cast<float*>(Cout) + row * ldc + col);
+          float4 o = make_float4(v[0], v[1], v[2], v[3]);
+          if (OUT == OUT_F32_ACC) {
+            const float4 old = *dst;
+            o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+          }
+          *dst = o;
+        }
+      }
+  }
+}
+
+// FP8 matrix-core path: one workgroup per output tile.
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_fp8_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
+    const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
+    int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
+  using C = Cfg<BM, BN, WM, WN, SB_MODE, PREC_FP8, NW, NS>;
   constexpr int T = C::T, MT = C::MT, NT = C::NT, ACC = C::ACC;
   // One distinct LDS object per pipeline stage (see the file comment).
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::kBufBytes];
@@ -218,157 +463,105 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     if (SB_MODE == SB_ROWS) ssb.issue(SB + (int64_t)lb * ldsb, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
   };
 
-  // One scale block: start filling `nxt` with block lb + NS - 1, multiply
-  // block lb from `cur`, then wait until block lb + 1 has landed (the fill
-  // just issued may stay in flight) and synchronise.
-  auto step = [&](const uint8_t* cur, uint8_t* nxt, int lb) {
-    const bool fill = lb + NS - 1 < nLB;
-    if (fill) stage_all(lb + NS - 1, nxt);
-    const uint8_t* ta = cur;
-    const uint8_t* tb = cur + BM * BK;
-    const float* lsa = reinterpret_cast<const float*>(cur + C::kSaOff);
-    const float* lsb = reinterpret_cast<const float*>(cur + C::kSbOff);
-    const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLB + lb] : 1.0f;
+  {
+    // One scale block: start filling `nxt` with block lb + NS - 1, multiply
+    // block lb from `cur`, then wait until block lb + 1 has landed (the fill
+    // just issued may stay in flight) and synchronise.
+    auto step = [&](const uint8_t* cur, uint8_t* nxt, int lb) {
+      const bool fill = lb + NS - 1 < nLB;
+      if (fill) stage_all(lb + NS - 1, nxt);
+      const uint8_t* ta = cur;
+      const uint8_t* tb = cur + BM * BK;
+      const float* lsa = reinterpret_cast<const float*>(cur + C::kSaOff);
+      const float* lsb = reinterpret_cast<const float*>(cur + C::kSbOff);
+      const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLB + lb] : 1.0f;
 
-    if (PREC == PREC_F16) {
-      // 32x32 sub-tiles.  Lane l: row (l % 32) of the sub-tile, half h = l / 32
-      // holds K bytes [64h, 64h + 64) of the block; MFMA k (k < 8) takes the
-      // 8 codes at 64h + 8k.  Outputs: column l % 32, rows 8q + 4h + u for
-      // accumulator 4q + u.  The MT x NT sub-tile products are built side by
-      // side, two K slices (one 16-byte LDS read per row) at a time, so the
-      // matrix core always has independent accumulation chains.
-      const int h = lane >> 5, rr = lane & 31;
-      v16f p[MT][NT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) p[mt][nt] = v16f{};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v8h a[MT][2], b[NT][2];
+      {
+        // 16x16 sub-tiles.  Lane l: row (l % 16), K bytes [32 (l / 16), +32).
+        // Outputs: column l % 16, rows 4 (l / 16) + u for accumulator u.
+        const int g = lane >> 4, rr = lane & 15;
+        v8i fa[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const uint4 v = lds16(ta, wm * WM + mt * 32 + rr, 4 * h + c);
-          a[mt][0] = cvt8(v.x, v.y);
-          a[mt][1] = cvt8(v.z, v.w);
+          const int row = wm * WM + mt * 16 + rr;
+          const uint4 lo = lds16(ta, row, 2 * g), hi = lds16(ta, row, 2 * g + 1);
+          fa[mt] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        float s[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float4 v = *reinterpret_cast<const float4*>(lsa + wm * WM + mt * 16 + 4 * g);
+          s[mt][0] = v.x * sblk; s[mt][1] = v.y * sblk; s[mt][2] = v.z * sblk; s[mt][3] = v.w * sblk;
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const uint4 v = lds16(tb, wn * WN + nt * 32 + rr, 4 * h + c);
-          b[nt][0] = cvt8(v.x, v.y);
-          b[nt][1] = cvt8(v.z, v.w);
-        }
+          const int col = wn * WN + nt * 16 + rr;
+          const uint4 lo = lds16(tb, col, 2 * g), hi = lds16(tb, col, 2 * g + 1);
+          const v8i fb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          const float sbc = (SB_MODE == SB_ROWS) ? lsb[col] : 1.0f;
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+          for (int mt = 0; mt < MT; ++mt) {
+            // E4M3 x E4M3 (format selectors 0, 0), no block scaling in the MFMA.
+            const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[mt], fb, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                           0, 0, 0, 0, 0, 0);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              p[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt][k], b[nt][k], p[mt][nt], 0, 0, 0);
-      }
-      // Rescale-accumulate.  Row scales of accumulator e: rows 8(e/4) + 4h + e%4.
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        float sr[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = *reinterpret_cast<const float4*>(lsa + wm * WM + mt * 32 + 8 * q + 4 * h);
-          sr[4 * q + 0] = v.x * sblk; sr[4 * q + 1] = v.y * sblk;
-          sr[4 * q + 2] = v.z * sblk; sr[4 * q + 3] = v.w * sblk;
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float sbc = (SB_MODE == SB_ROWS) ? lsb[wn * WN + nt * 32 + rr] : 1.0f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float sc = (SB_MODE == SB_ROWS) ? sr[e] * sbc : sr[e];
-            acc[mt][nt][e] = fmaf(p[mt][nt][e], sc, acc[mt][nt][e]);
+            for (int e = 0; e < 4; ++e) {
+              const float sc = (SB_MODE == SB_ROWS) ? s[mt][e] * sbc : s[mt][e];
+              acc[mt][nt][e] = fmaf(p[e], sc, acc[mt][nt][e]);
+            }
           }
         }
+      }
+      if (NS == 3 && fill)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));   // block lb+1 landed, lb+2 may fly
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();                    // everyone's fill landed; `cur` may be refilled
+    };
+
+    stage_all(0, lds0);
+    if (NS == 3 && nLB > 1) {
+      stage_all(1, lds1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    lds_barrier();
+    if (NS == 2) {
+      for (int lb = 0; lb < nLB; lb += 2) {
+        step(lds0, lds1, lb);
+        if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
       }
     } else {
-      // 16x16 sub-tiles.  Lane l: row (l % 16), K bytes [32 (l / 16), +32).
-      // Outputs: column l % 16, rows 4 (l / 16) + u for accumulator u.
-      const int g = lane >> 4, rr = lane & 15;
-      v8i fa[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * WM + mt * 16 + rr;
-        const uint4 lo = lds16(ta, row, 2 * g), hi = lds16(ta, row, 2 * g + 1);
-        fa[mt] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int lb = 0; lb < nLB; lb += 3) {
+        step(lds0, lds2, lb);
+        if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
+        if (lb + 2 < nLB) step(lds2, lds1, lb + 2);
       }
-      float s[MT][4];
+    }
+  }
+
+  // Epilogue.
+  {
+    // Row of accumulator e in sub-tile mt, column of sub-tile nt.
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float4 v = *reinterpret_cast<const float4*>(lsa + wm * WM + mt * 16 + 4 * g);
-        s[mt][0] = v.x * sblk; s[mt][1] = v.y * sblk; s[mt][2] = v.z * sblk; s[mt][3] = v.w * sblk;
-      }
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int col = wn * WN + nt * 16 + rr;
-        const uint4 lo = lds16(tb, col, 2 * g), hi = lds16(tb, col, 2 * g + 1);
-        const v8i fb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const float sbc = (SB_MODE == SB_ROWS) ? lsb[col] : 1.0f;
+      for (int e = 0; e < ACC; ++e) {
+        const int64_t row = i0 + wm * WM + mt * T + 4 * (lane >> 4) + e;
+        if (row >= I) continue;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          // E4M3 x E4M3 (format selectors 0, 0), no block scaling in the MFMA.
-          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[mt], fb, v4f{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sc = (SB_MODE == SB_ROWS) ? s[mt][e] * sbc : s[mt][e];
-            acc[mt][nt][e] = fmaf(p[e], sc, acc[mt][nt][e]);
+        for (int nt = 0; nt < NT; ++nt) {
+          const int64_t col = j0 + wn * WN + nt * T + (lane & (T - 1));
+          const float v = acc[mt][nt][e];
+          if (OUT == OUT_F32) {
+            static_cast<float*>(Cout)[row * ldc + col] = v;
+          } else if (OUT == OUT_F32_ACC) {
+            float* p = static_cast<float*>(Cout) + row * ldc + col;
+            *p = *p + v;
+          } else {
+            static_cast<uint16_t*>(Cout)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(v);
           }
-        }
-      }
-    }
-    if (NS == 3 && fill)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));   // block lb+1 landed, lb+2 may fly
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();                  // everyone's fill landed; `cur` may be refilled
-  };
-
-  stage_all(0, lds0);
-  if (NS == 3 && nLB > 1) {
-    stage_all(1, lds1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  }
-  __syncthreads();
-  if (NS == 2) {
-    for (int lb = 0; lb < nLB; lb += 2) {
-      step(lds0, lds1, lb);
-      if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
-    }
-  } else {
-    for (int lb = 0; lb < nLB; lb += 3) {
-      step(lds0, lds2, lb);
-      if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
-      if (lb + 2 < nLB) step(lds2, lds1, lb + 2);
-    }
-  }
-
-  // Epilogue.  Row of accumulator e in sub-tile mt, column of sub-tile nt.
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int e = 0; e < ACC; ++e) {
-      const int rloc = (PREC == PREC_F16) ? 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) : 4 * (lane >> 4) + e;
-      const int64_t row = i0 + wm * WM + mt * T + rloc;
-      if (row >= I) continue;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int64_t col = j0 + wn * WN + nt * T + (lane & (T - 1));
-        const float v = acc[mt][nt][e];
-        if (OUT == OUT_F32) {
-          static_cast<float*>(Cout)[row * ldc + col] = v;
-        } else if (OUT == OUT_F32_ACC) {
-          float* p = static_cast<float*>(Cout) + row * ldc + col;
-          *p = *p + v;
-        } else {
-          static_cast<uint16_t*>(Cout)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(v);
         }
       }
     }
@@ -385,16 +578,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void* __restrict__ C, in
   }
 }
 
+constexpr int kCUs = 256;   // MI355X compute units
+
 template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS>
 void launch_cfg(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                 const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
                 int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
   const int tilesM = (int)((I + BM - 1) / BM), tilesN = (int)(J / BN);
-  hipLaunchKernelGGL((block_gemm_kernel<BM, BN, WM, WN, SB_MODE, OUT, PREC, NW, NS>), dim3(tilesM * tilesN),
-                     dim3(64 * NW), 0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+  const int nTiles = tilesM * tilesN;
+  if (PREC == PREC_F16) {
+    hipLaunchKernelGGL((block_gemm_f16_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS>), dim3(nTiles), dim3(64 * NW), 0,
+                       st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+  } else {
+    hipLaunchKernelGGL((block_gemm_fp8_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS>), dim3(nTiles), dim3(64 * NW), 0,
+                       st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+  }
 }
-
-constexpr int kCUs = 256;   // MI355X compute units
 
 // Tile choice: 256 x 128 output tiles (8 waves of 64 x 64, triple-buffered
 // LDS, one workgroup per CU) when they still give every CU a tile; otherwise
