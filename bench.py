@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--no-fp8-path", action="store_true", help="skip timing the FP8 matrix-core GEMM path")
+    ap.add_argument("--no-bf16-baseline", action="store_true", help="skip timing the BF16 GEMMs of the same shapes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -144,6 +145,54 @@ def cpu_baseline(W, layers, sample_tokens):
                       f"tokens, numpy float64 oracle, {dt:.1f} s"}
 
 
+def bf16_baseline(torch, B, layers, steps, warmup, fp8_gemm_ms, fp8_step_ms, fp8_mc_gemm_ms):
+    """The same 12 GEMM shapes in plain BF16: this library's BF16 kernel and hipBLASLt (torch.mm).
+
+    For every linear: forward [M, k] x [n, k]^T, dgrad [M, n] x [k, n]^T and
+    wgrad [n, M] x [k, M]^T, each as C = A . B^T with BF16 operands resident
+    in HBM.  hipBLASLt gets the second operand pre-transposed ([L, J]
+    row-major, prepared outside the timed region).  Ratios > 1 mean the FP8
+    path is faster.
+    """
+    ops = []
+    for L in layers:
+        dyT = L.dy.t().contiguous()
+        xT = L.x.t().contiguous()
+        wT = L.w.t().contiguous()
+        for a, b in ((L.x, L.w), (L.dy, wT), (dyT, xT)):
+            ops.append((a, b, b.t().contiguous(), torch.empty((a.shape[0], b.shape[0]), dtype=torch.bfloat16,
+                                                              device=a.device)))
+    flops = sum(2 * a.shape[0] * b.shape[0] * a.shape[1] for a, b, _, _ in ops)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def run(fn):
+        for _ in range(warmup):
+            for op in ops:
+                fn(*op)
+        torch.cuda.synchronize()
+        evs = [[(mk(), mk()) for _ in ops] for _ in range(steps)]
+        for s in range(steps):
+            for (e0, e1), op in zip(evs[s], ops):
+                e0.record()
+                fn(*op)
+                e1.record()
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for row in evs for e0, e1 in row) / steps
+
+    own_ms = run(lambda a, b, bt, c: B.bf16_gemm_nt(a, b, c=c))
+    blas_ms = run(lambda a, b, bt, c: torch.mm(a, bt, out=c))
+    out = {"gemm_gflop_per_step": round(flops / 1e9, 3),
+           "own_kernel": {"gemm_ms_per_step": round(own_ms, 4), "tflops": round(flops / (own_ms * 1e-3) / 1e12, 1)},
+           "hipblaslt": {"gemm_ms_per_step": round(blas_ms, 4), "tflops": round(flops / (blas_ms * 1e-3) / 1e12, 1)},
+           "speedup_fp8_exact_gemms_vs_own_bf16": round(own_ms / fp8_gemm_ms, 3),
+           "speedup_fp8_exact_gemms_vs_hipblaslt": round(blas_ms / fp8_gemm_ms, 3),
+           "speedup_fp8_exact_step_vs_hipblaslt_gemms": round(blas_ms / fp8_step_ms, 3),
+           "note": "BF16 GEMMs of the same 12 shapes; the FP8 step includes its quantisers"}
+    if fp8_mc_gemm_ms is not None:
+        out["speedup_fp8_matrix_core_gemms_vs_hipblaslt"] = round(blas_ms / fp8_mc_gemm_ms, 3)
+    return out
+
+
 def copy_probe(torch, dev, mib):
     """A plain device copy of known size (float32 multiply by one), launched once.
 
@@ -226,6 +275,7 @@ def main():
         traffic = float(tr["gemm_hbm_bytes_per_launch"])
 
     fast = None
+    f_gemm_ms = None
     if not args.no_fp8_path:
         f_ms, f_gemm, f_q, _ = timed(True)
         f_gemm_ms = sum(sum(r) for r in f_gemm)
@@ -268,6 +318,8 @@ def main():
         "wall_s_timed": round(t_wall, 3),
         "fp8_matrix_core_path": fast,
     }
+    if not args.no_bf16_baseline:
+        out["bf16_baseline"] = bf16_baseline(torch, B, layers, args.steps, args.warmup, gemm_ms, ms_step, f_gemm_ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, layers, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

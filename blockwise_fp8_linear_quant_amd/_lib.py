@@ -24,6 +24,7 @@ SIGNATURES = {
                                     _vp, _i64, _i32, _vp, _sz, _vp]),
     "fp8_block_gemm": (_i32, [_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
                               _vp, _i64, _i32, _i32, _vp, _sz, _vp]),
+    "bf16_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _i32, _vp]),
     "fp8_block_gemm_workspace_size": (_sz, [_i32, _i64, _i64, _i64]),
     "fp8_e4m3_encode": (_i32, [_vp, _vp, _i64, _vp]),
     "fp8blk_status_string": (ctypes.c_char_p, [_i32]),

@@ -175,6 +175,21 @@ def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False
     return dw
 
 
+def bf16_gemm_nt(a, b, out_dtype=torch.bfloat16, c=None):
+    """C[M, N] = A[M, K] . B[N, K]^T over BF16 operands (the BF16 baseline GEMM)."""
+    _check_2d(a, torch.bfloat16, "a")
+    _check_2d(b, torch.bfloat16, "b")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must have the same number of columns")
+    c = _out((M, N), out_dtype, a.device, c)
+    st = _lib.load().bf16_gemm_nt(_ptr(a), a.stride(0), _ptr(b), b.stride(0), M, N, K,
+                                  _ptr(c), c.stride(0), _dtype_code(c), _stream(a))
+    _lib.check(st, "bf16_gemm_nt")
+    return c
+
+
 def fp8_e4m3_encode(x, q=None):
     """Elementwise binary32 -> E4M3 codes with the library's device encoder."""
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():

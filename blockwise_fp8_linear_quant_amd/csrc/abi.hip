@@ -183,6 +183,26 @@ int fp8_block_gemm(int op, int flags, const uint8_t* a, int64_t ld_a, const floa
                    static_cast<hipStream_t>(stream));
 }
 
+int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,
+                 int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8BLK_INVALID_ARG;
+  if (c_dtype != FP8BLK_OUT_F32 && c_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
+  if (N % 128 != 0 || K % 64 != 0) return FP8BLK_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0) return FP8BLK_OK;
+  if (c == nullptr || ld_c < N) return FP8BLK_INVALID_ARG;
+  const int out = c_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
+  if (!al16(c) || ld_c % (out == OUT_BF16 ? 8 : 4) != 0) return FP8BLK_MISALIGNED;
+  if (K > 0) {
+    if (a == nullptr || b == nullptr || ld_a < K || ld_b < K) return FP8BLK_INVALID_ARG;
+    if (!al16(a) || !al16(b) || ld_a % 8 != 0 || ld_b % 8 != 0) return FP8BLK_MISALIGNED;
+    if (M * ld_a * 2 >= (int64_t)1 << 31 || N * ld_b * 2 >= (int64_t)1 << 31) return FP8BLK_UNSUPPORTED_SHAPE;
+  }
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_bf16_gemm(static_cast<const uint16_t*>(a), ld_a, static_cast<const uint16_t*>(b), ld_b, M, N, K, c, ld_c,
+                   out, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
 size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
   (void)op; (void)M; (void)N; (void)K;
   return 0;

@@ -568,6 +568,135 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   }
 }
 
+// Plain BF16 GEMM  C[i, j] = sum_l A[i, l] B[j, l]  (both operands BF16,
+// contraction-contiguous), the comparator for the block-scaled FP8 GEMMs on
+// the same shapes.  Same structure as the exact path: 64-element K stages of
+// 128-byte rows staged straight into LDS (three buffers), K slices read one
+// ahead of the multiply, v_mfma_f32_32x32x16_bf16 accumulating directly into
+// the FP32 accumulators (no per-block scale), transposed sub-tiles and the same
+// epilogue.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+constexpr int BK16 = 64;   // BF16 elements per K stage (128 bytes per row)
+
+template <int BM, int BN, int WM, int WN, int OUT, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void bf16_gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
+  constexpr int WGN = BN / WN;
+  constexpr int MT = WM / 32, NT = WN / 32;
+  static_assert((BM / WM) * WGN == NW, "one wave per WM x WN sub-tile");
+  constexpr int kBuf = (BM + BN) * BK;   // bytes per stage: 128-byte rows
+  constexpr int kVmem = TileStager<BM, NW>::kLoads + TileStager<BN, NW>::kLoads;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[NS == 3 ? kBuf : 16];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  int tm, tn;
+  map_tile(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int nLB = (int)(L / BK16);
+  // Lane l: row (l % 32) of a 32x32 sub-tile; half h = l / 32 holds elements
+  // [32h, 32h + 32) of the stage; slice c (0..3) is the 8 elements at 32h + 8c,
+  // one MFMA operand.  Output layout as in the exact FP8 path.
+  const int h = lane >> 5, rr = lane & 31;
+
+  v16f acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v16f{};
+
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(A);
+  const uint8_t* Bb = reinterpret_cast<const uint8_t*>(B);
+  TileStager<BM, NW> sta;
+  TileStager<BN, NW> stb;
+  sta.init(lda * 2, i0, I - 1, wave, lane);
+  stb.init(ldb * 2, j0, j0 + BN - 1, wave, lane);
+  auto stage_all = [&](int lb, uint8_t* buf) {
+    sta.issue(Ab + (int64_t)lb * BK, buf, wave);
+    stb.issue(Bb + (int64_t)lb * BK, buf + BM * BK, wave);
+  };
+  uint4 qa[2][MT], qb[2][NT];
+  auto load_slice = [&](const uint8_t* buf, int c, int slot) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) qa[slot][mt] = lds16(buf, wm * WM + mt * 32 + rr, 4 * h + c);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) qb[slot][nt] = lds16(buf + BM * BK, wn * WN + nt * 32 + rr, 4 * h + c);
+  };
+  auto multiply = [&](int slot) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, qb[slot][nt]),
+                                                               __builtin_bit_cast(v8bf, qa[slot][mt]), acc[mt][nt], 0, 0, 0);
+  };
+  auto step = [&](uint8_t* cur, const uint8_t* nxt, int lb) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      load_slice(cur, c + 1, (c + 1) & 1);
+      multiply(c & 1);
+    }
+    if (NS == 3 && lb + 2 < nLB)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kVmem));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // The slice-3 registers must hold their data before `cur` is refilled.
+    lds_barrier();
+    if (lb + NS < nLB) stage_all(lb + NS, cur);
+    // Slice 3 sits in slot 1; slice 0 of the next stage goes to slot 0.
+    if (lb + 1 < nLB) load_slice(nxt, 0, 0);
+    multiply(1);
+  };
+  const int pre = nLB < NS ? nLB : NS;
+  stage_all(0, lds0);
+  if (pre > 1) stage_all(1, lds1);
+  if (NS == 3 && pre > 2) stage_all(2, lds2);
+  if (NS == 3 && pre > 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kVmem));
+  else if (pre > 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kVmem));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  load_slice(lds0, 0, 0);
+  if (NS == 2) {
+    for (int lb = 0; lb < nLB; lb += 2) {
+      step(lds0, lds1, lb);
+      if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
+    }
+  } else {
+    for (int lb = 0; lb < nLB; lb += 3) {
+      step(lds0, lds1, lb);
+      if (lb + 1 < nLB) step(lds1, lds2, lb + 1);
+      if (lb + 2 < nLB) step(lds2, lds0, lb + 2);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t row = i0 + wm * WM + mt * 32 + rr;
+    if (row >= I) continue;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = j0 + wn * WN + nt * 32 + 8 * q + 4 * h;
+        const v16f& v = acc[mt][nt];
+        if (OUT == OUT_BF16) {
+          const uint32_t lo = f32_to_bf16_rne(v[4 * q]) | (f32_to_bf16_rne(v[4 * q + 1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[4 * q + 2]) | (f32_to_bf16_rne(v[4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + row * ldc + col) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(Cout) + row * ldc + col) =
+              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+      }
+  }
+}
+
 template <int OUT>
 __global__ __launch_bounds__(256) void fill_zero_kernel(void* __restrict__ C, int64_t rows, int64_t cols, int64_t ldc) {
   const int64_t n = rows * cols;
@@ -609,6 +738,20 @@ void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
     launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC, 4, 2>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
 }
 
+template <int OUT>
+void launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t I, int64_t J, int64_t L,
+                 void* C, int64_t ldc, hipStream_t st) {
+  if (((I + 255) / 256) * (J / 128) >= kCUs) {
+    const int tm = (int)((I + 255) / 256), tn = (int)(J / 128);
+    hipLaunchKernelGGL((bf16_gemm_kernel<256, 128, 64, 64, OUT, 8, 3>), dim3(tm * tn), dim3(512), 0, st,
+                       A, lda, B, ldb, I, L, C, ldc, tm, tn);
+  } else {
+    const int tm = (int)((I + 127) / 128), tn = (int)(J / 128);
+    hipLaunchKernelGGL((bf16_gemm_kernel<128, 128, 64, 64, OUT, 4, 2>), dim3(tm * tn), dim3(256), 0, st,
+                       A, lda, B, ldb, I, L, C, ldc, tm, tn);
+  }
+}
+
 }  // namespace
 
 void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
@@ -638,6 +781,23 @@ void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t l
   FP8BLK_GEMM_CASE(SB_ROWS, OUT_F32)
   FP8BLK_GEMM_CASE(SB_ROWS, OUT_F32_ACC)
 #undef FP8BLK_GEMM_CASE
+}
+
+void launch_bf16_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                      int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode, hipStream_t st) {
+  if (L == 0) {
+    const int64_t n = I * J;
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    if (out_mode == OUT_BF16)
+      hipLaunchKernelGGL(fill_zero_kernel<OUT_BF16>, dim3(blocks), dim3(256), 0, st, C, I, J, ldc);
+    else
+      hipLaunchKernelGGL(fill_zero_kernel<OUT_F32>, dim3(blocks), dim3(256), 0, st, C, I, J, ldc);
+    return;
+  }
+  if (out_mode == OUT_BF16)
+    launch_bf16<OUT_BF16>(A, lda, B, ldb, I, J, L, C, ldc, st);
+  else
+    launch_bf16<OUT_F32>(A, lda, B, ldb, I, J, L, C, ldc, st);
 }
 
 }  // namespace fp8blk

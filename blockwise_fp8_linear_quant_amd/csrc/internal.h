@@ -29,4 +29,9 @@ void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t l
                        int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode,
                        int prec, hipStream_t st);
 
+// C[I, J] = sum_l A[i, l] B[j, l] over BF16 operands (A [I, lda], B [J, ldb]);
+// J a multiple of 128, L a multiple of 64; out_mode OUT_F32 or OUT_BF16.
+void launch_bf16_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                      int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode, hipStream_t st);
+
 }  // namespace fp8blk

@@ -186,6 +186,22 @@ int fp8_block_gemm(int op, int flags, const uint8_t* a, int64_t ld_a, const floa
                    int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, int accumulate,
                    void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Plain BF16 GEMM  C[M, N] = A[M, K] . B[N, K]^T  (no quantisation, FP32
+ * accumulation), the BF16 baseline against which the FP8 GEMMs are compared:
+ * the pages report the FP8 recipe's throughput relative to BF16 training
+ * (paperlayer.ai Puro-2B summary, appendix D "MuonH Scaling-Ladder Analysis",
+ * 1.36x at 1.7B; ailog.hnlab.kr post, FP8 linear layers are 72% of compute).
+ * a [M, ld_a >= K], b [N, ld_b >= K] BF16 bit patterns, row-major, 16-byte
+ * aligned, ld_a and ld_b multiples of 8 elements; c [M, ld_c >= N], FP32 or
+ * BF16 (c_dtype, rounded to nearest even), 16-byte aligned, ld_c a multiple
+ * of 4 (FP32) or 8 (BF16).  N must be a multiple of 128 and K of 64 (else
+ * FP8BLK_UNSUPPORTED_SHAPE); M is arbitrary; K = 0 writes zeros.  Row offsets
+ * (M * ld_a and N * ld_b, in bytes) must stay below 2 GiB.
+ */
+int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,
+                 int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, void* stream);
+
 /* Workspace bytes a GEMM call needs for (op, M, N, K); 0 means none. */
 size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K);
 

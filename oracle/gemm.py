@@ -30,7 +30,7 @@ Operand mapping (row-major shapes, X [M, K], W [N, K], dY [M, N]):
 import numpy as np
 
 from . import e4m3
-from .quant import GROUP, expand_block_scales
+from .quant import GROUP, bf16_bits_to_f32, expand_block_scales
 
 
 def _deq(codes, row_scales):
@@ -75,6 +75,22 @@ def wgrad(dyqt, sdyt, xqt, sxt, rows=None, cols=None, budget=True):
     dyqt [N, M], sdyt [N, ceil(M/128)], xqt [K, M], sxt [K, ceil(M/128)].
     """
     return block_gemm(dyqt, sdyt, xqt, sxt, rows, cols, budget)
+
+
+def bf16_gemm(a_bits, b_bits, rows=None, cols=None, budget=True):
+    """Plain BF16 GEMM C = A . B^T in float64 (the baseline the FP8 GEMMs are compared with).
+
+    Pages: paperlayer.ai summary, appendix D "MuonH Scaling-Ladder Analysis"
+    (FP8 throughput relative to BF16 at 1.7B) -- the BF16 GEMM of the same
+    shapes is the reference point.  a_bits [I, L], b_bits [J, L] are BF16 bit
+    patterns; every BF16 value is exact in float64.  Returns (C, Bnd) with
+    Bnd = |A| @ |B|^T (None when budget=False).
+    """
+    a = bf16_bits_to_f32(a_bits if rows is None else a_bits[rows]).astype(np.float64)
+    b = bf16_bits_to_f32(b_bits if cols is None else b_bits[cols]).astype(np.float64)
+    c = a @ b.T
+    bnd = (np.abs(a) @ np.abs(b).T) if budget else None
+    return c, bnd
 
 
 def round_to_bf16(y):

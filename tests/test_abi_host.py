@@ -22,13 +22,14 @@ def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
-    return sorted(set(n for n in names if n.startswith("fp8")))
+    return sorted(set(n for n in names if n.startswith(("fp8", "bf16"))))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_block_gemm_fwd", "fp8_block_gemm_dgrad",
-              "fp8_block_gemm_wgrad", "fp8_block_gemm_workspace_size", "fp8blk_status_string"):
+              "fp8_block_gemm_wgrad", "fp8_block_gemm_workspace_size", "fp8blk_status_string",
+              "bf16_gemm_nt"):
         assert n in names
 
 
@@ -112,3 +113,20 @@ def test_generic_gemm_validation():
     assert lib.fp8_block_gemm(0, 1, P, 256, P, 16, P, 256, P, 0, 16, 200, 256, P, 256, 0, 0, None, 0, None) == 2
     assert lib.fp8_block_gemm(0, 1, None, 0, None, 0, None, 0, None, 0, 0, 256, 256, None, 0, 0, 0, None, 0,
                               None) == 0
+
+
+def test_bf16_gemm_validation():
+    lib = _lib()
+    P = ctypes.c_void_p(16)
+    # bad dtype, negative size, N not a multiple of 128, K not a multiple of 64
+    assert lib.bf16_gemm_nt(P, 64, P, 64, 16, 128, 64, P, 128, 5, None) == 1
+    assert lib.bf16_gemm_nt(P, 64, P, 64, -1, 128, 64, P, 128, 0, None) == 1
+    assert lib.bf16_gemm_nt(P, 64, P, 64, 16, 100, 64, P, 128, 0, None) == 2
+    assert lib.bf16_gemm_nt(P, 96, P, 96, 16, 128, 96, P, 128, 0, None) == 2
+    # leading dimensions: too small, not a multiple of 8 elements, misaligned pointer
+    assert lib.bf16_gemm_nt(P, 32, P, 64, 16, 128, 64, P, 128, 0, None) == 1
+    assert lib.bf16_gemm_nt(P, 68, P, 64, 16, 128, 64, P, 128, 0, None) == 3
+    assert lib.bf16_gemm_nt(ctypes.c_void_p(18), 64, P, 64, 16, 128, 64, P, 128, 0, None) == 3
+    assert lib.bf16_gemm_nt(P, 64, P, 64, 16, 128, 64, P, 132, 1, None) == 3
+    # empty outputs are no-ops
+    assert lib.bf16_gemm_nt(None, 0, None, 0, 0, 128, 64, None, 0, 0, None) == 0

@@ -230,3 +230,41 @@ def test_acceptance_checks_reject_planted_errors():
     gb2[3] += 2                       # two BF16 ulps away
     ok, rep = compare.check_bf16(gb2, y, bnd * 1e-9)
     assert not ok and rep["bad"] == 1
+
+
+def _exact_bf16_gemm(a_bits, b_bits):
+    """sum_l A[i, l] * B[j, l] over the BF16 values with Fractions (tiny shapes only)."""
+    fa = bits_f32(a_bits)
+    fb = bits_f32(b_bits)
+    I, L = fa.shape
+    J = fb.shape[0]
+    out = [[sum((Fraction(float(fa[i, l])) * Fraction(float(fb[j, l])) for l in range(L)), Fraction(0))
+            for j in range(J)] for i in range(I)]
+    return out
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 64), (6, 2, 130)])
+def test_bf16_gemm_matches_exact_rational_sum(shape):
+    I, J, L = shape
+    rng = np.random.default_rng(7 + sum(shape))
+    a = to_bf16_trunc(rng.standard_normal((I, L)) * np.exp(rng.standard_normal((I, 1)) * 4))
+    b = to_bf16_trunc(rng.standard_normal((J, L)))
+    y, bnd = gemm.bf16_gemm(a, b)
+    ey = _exact_bf16_gemm(a, b)
+    for i in range(I):
+        for j in range(J):
+            assert abs(Fraction(float(y[i, j])) - ey[i][j]) <= Fraction(float(bnd[i, j])) * Fraction(1, 10 ** 12)
+
+
+def test_bf16_gemm_operand_orientation():
+    """C = A . B^T: a row of ones against a one-hot row of B picks one column of A."""
+    I, J, L = 4, 3, 8
+    a = to_bf16_trunc(np.arange(I * L, dtype=np.float32).reshape(I, L))
+    b = np.zeros((J, L), dtype=np.uint16)
+    for j in range(J):
+        b[j, 2 * j + 1] = 0x3F80          # BF16 1.0
+    y, _ = gemm.bf16_gemm(a, b)
+    want = np.arange(I * L, dtype=np.float64).reshape(I, L)[:, [1, 3, 5]]
+    assert np.array_equal(y, want)
+    ysel, _ = gemm.bf16_gemm(a, b, rows=np.array([2]), cols=np.array([1, 2]))
+    assert np.array_equal(ysel, want[[2]][:, [1, 2]])
