@@ -3,8 +3,8 @@
 One step = one decoder layer's linear work at M tokens (default 4096, hidden
 2048, intermediate 6144), everything the path computes:
   for each linear (qkv, o, gate_up, down):
-    quantise X (1x128 row-wise and token-dimension), W (128x128 with the
-    transposed copy) and dY (row-wise and token-dimension), then
+    quantise X (1x128 row-wise and token-dimension, both from one read), W
+    (128x128 with the transposed copy) and dY (both orientations, one read), then
     forward Y = X W^T (BF16 out), dgrad dX = dY W (BF16 out),
     wgrad dW = dY^T X (FP32 out).
 Inputs are seeded synthetic BF16 tensors (X ~ N(0,1), W ~ N(0,0.02),
@@ -88,19 +88,28 @@ class LayerBuffers:
         wgrad = n * mp + k * mp + 4 * (n + k) * (mp // 128) + 4 * n * k
         return [fwd, dgrad, wgrad]
 
-    def quant_bytes(self):
+    def quant_bytes(self, dual=True):
+        """Algorithmic HBM bytes of the step's quantisers (inputs read once per kernel)."""
         M, n, k = self.M, self.n, self.k
         row = lambda r, c: r * c * 3 + r * (-(-c // 128)) * 4          # 2 B in, 1 B out, scales
         tok = lambda r, c: r * c * 2 + c * (-(-r // 128) * 128) + c * (-(-r // 128)) * 4
         blk = n * k * 2 + 2 * n * k + 2 * 4 * (-(-n // 128)) * (-(-k // 128))
-        return row(M, k) + tok(M, k) + blk + row(M, n) + tok(M, n)
+        both = row(M, k) + tok(M, k) + row(M, n) + tok(M, n)
+        return blk + (both - 2 * M * k - 2 * M * n if dual else both)
 
-    def quantise(self, B):
-        B.fp8_quant_1x128(self.x, q=self.xq, scales=self.sx)
-        B.fp8_quant_1x128(self.x, transpose_out=True, q=self.xqT, scales=self.sxT)
+    def quantise(self, B, dual=True):
+        """All quantisers of the step; `dual` makes both 1x128 orientations of X and dY from one read."""
+        if dual:
+            B.fp8_quant_1x128_dual(self.x, self.xq, self.sx, self.xqT, self.sxT)
+        else:
+            B.fp8_quant_1x128(self.x, q=self.xq, scales=self.sx)
+            B.fp8_quant_1x128(self.x, transpose_out=True, q=self.xqT, scales=self.sxT)
         B.fp8_quant_128x128(self.w, True, self.wq, self.sw, self.wqT, self.swT)
-        B.fp8_quant_1x128(self.dy, q=self.dyq, scales=self.sdy)
-        B.fp8_quant_1x128(self.dy, transpose_out=True, q=self.dyqT, scales=self.sdyT)
+        if dual:
+            B.fp8_quant_1x128_dual(self.dy, self.dyq, self.sdy, self.dyqT, self.sdyT)
+        else:
+            B.fp8_quant_1x128(self.dy, q=self.dyq, scales=self.sdy)
+            B.fp8_quant_1x128(self.dy, transpose_out=True, q=self.dyqT, scales=self.sdyT)
 
     def gemms(self, B, fp8_mc=False, ev=None):
         """The three GEMMs; `ev` (4 events) brackets each launch when given."""
@@ -228,7 +237,7 @@ def main():
         for i, L in enumerate(layers):
             if evs is not None:
                 evs[i][0].record()
-            L.quantise(B)
+            L.quantise(B, dual=True)
             L.gemms(B, fp8_mc, evs[i][1:] if evs is not None else None)
 
     def timed(fp8_mc):
@@ -268,6 +277,24 @@ def main():
         for op, ms, fl in zip(("fwd", "dgrad", "wgrad"), row, L.gemm_flops()):
             gemms[f"{op}_{L.name}"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
     qbytes = sum(L.quant_bytes() for L in layers)
+
+    # The same quantiser outputs from the separate row-wise and token-dimension
+    # kernels (two reads of X and dY), for comparison with the single-read path.
+    def quant_only(dual):
+        for _ in range(args.warmup):
+            for L in layers:
+                L.quantise(B, dual)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            for L in layers:
+                L.quantise(B, dual)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+    sep_ms = quant_only(False)
+    sep_bytes = sum(L.quant_bytes(False) for L in layers)
 
     traffic = None
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY))
@@ -314,7 +341,10 @@ def main():
         "quantisers": {"ms_per_step": round(quant_ms, 4), "algorithmic_gb": round(qbytes / 1e9, 4),
                        "gbps": round(qbytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms > 0 else None,
                        "frac_hbm_peak": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-                       if quant_ms > 0 else None},
+                       if quant_ms > 0 else None,
+                       "path": "single-read dual 1x128 quantiser for X and dY + 128x128 for W",
+                       "separate_kernels": {"ms_per_step": round(sep_ms, 4), "algorithmic_gb": round(sep_bytes / 1e9, 4),
+                                            "gbps": round(sep_bytes / (sep_ms * 1e-3) / 1e9, 1)}},
         "wall_s_timed": round(t_wall, 3),
         "fp8_matrix_core_path": fast,
     }

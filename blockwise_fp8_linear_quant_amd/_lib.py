@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 SIGNATURES = {
     "fp8_quant_1x128": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp]),
+    "fp8_quant_1x128_dual": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "fp8_quant_128x128": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp]),
     "fp8_block_gemm_fwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
                                   _vp, _i64, _i32, _vp, _sz, _vp]),

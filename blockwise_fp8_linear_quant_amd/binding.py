@@ -77,6 +77,29 @@ def fp8_quant_1x128(x, transpose_out=False, q=None, scales=None):
     return q, scales
 
 
+def fp8_quant_1x128_dual(x, q=None, scales=None, qT=None, scalesT=None):
+    """Row-wise and token-dimension 1x128 quantisation of x from one read.
+
+    Returns (q, scales, qT, scalesT), identical to fp8_quant_1x128(x) and
+    fp8_quant_1x128(x, transpose_out=True).
+    """
+    _check_2d(x, torch.bfloat16, "x")
+    R, C = x.shape
+    if q is None:
+        q = _codes(R, C, x.device)
+    if scales is None:
+        scales = _scales(-(-C // 128), R, x.device)
+    if qT is None:
+        qT = torch.empty((C, _round_up(R, 128)), dtype=torch.uint8, device=x.device)
+    if scalesT is None:
+        scalesT = _scales(-(-R // 128), C, x.device)
+    st = _lib.load().fp8_quant_1x128_dual(
+        _ptr(x), R, C, x.stride(0), _ptr(q), q.stride(0), _ptr(scales), scales.stride(0),
+        _ptr(qT), qT.stride(0), _ptr(scalesT), scalesT.stride(0), _stream(x))
+    _lib.check(st, "fp8_quant_1x128_dual")
+    return q, scales, qT, scalesT
+
+
 def fp8_quant_128x128(w, with_transpose=False, q=None, scales=None, qT=None, scalesT=None):
     """128x128 block quantisation of BF16 w [rows, cols] -> (q, scales, qT, scalesT)."""
     _check_2d(w, torch.bfloat16, "w")

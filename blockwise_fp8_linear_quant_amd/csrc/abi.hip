@@ -82,6 +82,24 @@ int fp8_quant_1x128(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x
   return finish();
 }
 
+int fp8_quant_1x128_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                         uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                         uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT, void* stream) {
+  if (rows < 0 || cols < 0) return FP8BLK_INVALID_ARG;
+  if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (x_bf16 == nullptr || q == nullptr || scales == nullptr || qT == nullptr || scalesT == nullptr)
+    return FP8BLK_INVALID_ARG;
+  const int64_t mpad = (rows + 127) / 128 * 128;
+  if (ld_x < cols || ld_q < cols || ld_s < rows || ld_qT < mpad || ld_sT < cols) return FP8BLK_INVALID_ARG;
+  if (!al16(x_bf16) || ld_x % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al16(qT) || ld_qT % 16 != 0 ||
+      !al4(scales) || !al4(scalesT))
+    return FP8BLK_MISALIGNED;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_quant_dual(static_cast<const uint16_t*>(x_bf16), rows, cols, ld_x, q, ld_q, scales, ld_s,
+                    qT, ld_qT, scalesT, ld_sT, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
 int fp8_quant_128x128(const void* w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
                       uint8_t* q, int64_t ld_q, float* scales,
                       uint8_t* qT, int64_t ld_qT, float* scalesT, void* stream) {

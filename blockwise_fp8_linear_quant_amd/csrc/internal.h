@@ -13,6 +13,9 @@ void launch_quant_tokens(const uint16_t* x, int64_t M, int64_t C, int64_t ldx,
 void launch_quant_blocks(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
                          uint8_t* q, int64_t ldq, float* s,
                          uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st);
+void launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                       uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st);
 void launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t st);
 
 // Scale modes of the second GEMM operand.

@@ -274,6 +274,119 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
   if (i < n) q[i] = (uint8_t)encode_any(x[i]);
 }
 
+// ---------------------------------------------------------------------------
+// Both 1x128 orientations from one read: a 256-thread workgroup takes a tile
+// of 128 rows (tokens) x 128 columns (features), thread (rb, c), rb = t/16,
+// c = t%16, holding rows [8rb, 8rb+8) x columns [8c, 8c+8) as in the block
+// quantiser.  Row maxima (groups along the columns) are reduced over the 16
+// lanes of a DPP row; column maxima (groups along the tokens) over lanes 16
+// and 32 apart and then across the 4 waves through LDS.  Each element is
+// encoded twice -- with its row's scale into q (row-wise layout) and with its
+// column's scale into qT (transposed, tokens contiguous) -- so the outputs are
+// those of the two separate quantisers, bit for bit, for 2 bytes read instead
+// of 4.  Token rows past R (up to the 128-padded length) read as zero and
+// come out as 0x00 pads in qT.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t code4_each(float a, float b, float c, float d, const GroupQ (&g)[8], int j0) {
+  // Four values of one row, columns j0..j0+3, each with its own column's scale.
+  const float q0 = g[j0 + 0].s == 0.0f ? 0.0f : group_quotient(a, g[j0 + 0]);
+  const float q1 = g[j0 + 1].s == 0.0f ? 0.0f : group_quotient(b, g[j0 + 1]);
+  const float q2 = g[j0 + 2].s == 0.0f ? 0.0f : group_quotient(c, g[j0 + 2]);
+  const float q3 = g[j0 + 3].s == 0.0f ? 0.0f : group_quotient(d, g[j0 + 3]);
+  return enc4(q0, q1, q2, q3);
+}
+
+__global__ __launch_bounds__(256) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT) {
+  __shared__ float cred[4][128];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t br = blockIdx.y, bc = blockIdx.x;
+  const int c = t & 15, rb = t >> 4;
+  const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + i;
+    v[i] = (r < R && c0 < C) ? load8(x + r * ldx, c0, C) : make_uint4(0, 0, 0, 0);
+  }
+  // Column maxima of this thread's 8 columns over its 8 rows, then over the
+  // 4 row blocks of the wave (lanes 16 and 32 apart), then over the waves.
+  float cm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(elem(v[i], j)));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    cm[j] = m;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cred[wave][c * 8 + j] = cm[j];
+  }
+  // Row maxima over the 16 lanes of a DPP row (the 128 columns of the tile).
+  float rm[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(v[i], j)));
+    m = max8(m);
+    rm[i] = dpp_fmax<kRor8>(m);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    cm[j] = fmaxf(fmaxf(cred[0][c * 8 + j], cred[1][c * 8 + j]), fmaxf(cred[2][c * 8 + j], cred[3][c * 8 + j]));
+
+  // Row-wise codes and scales.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const GroupQ gq = group_setup(rm[i]);
+    const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
+    const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gq);
+    const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gq);
+    const int64_t r = r0 + i;
+    if (r < R && c0 < C) {
+      store8(q + r * ldq + c0, c0, C, lo, hi);
+      if (c == 0) s[bc * lds + r] = gq.s;
+    }
+  }
+  // Token-dimension codes: row-major words with per-column scales, then 4x4
+  // byte transposes into words of 4 tokens each.
+  GroupQ gc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gc[j] = group_setup(cm[j]);
+  uint32_t rw[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    rw[i][0] = code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
+    rw[i][1] = code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
+  }
+  uint32_t cw[8][2];
+#pragma unroll
+  for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t rr4[4] = {rw[4 * rb2][hh], rw[4 * rb2 + 1][hh], rw[4 * rb2 + 2][hh], rw[4 * rb2 + 3][hh]};
+      uint32_t cc[4];
+      transpose4x4(rr4, cc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cw[4 * hh + j][rb2] = cc[j];
+    }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (c0 + j < C) {
+      *reinterpret_cast<uint2*>(qT + (c0 + j) * ldqT + r0) = make_uint2(cw[j][0], cw[j][1]);
+      if (rb == 0) sT[br * ldsT + c0 + j] = gc[j].s;
+    }
+  }
+}
+
 }  // namespace
 
 void launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
@@ -293,6 +406,13 @@ void launch_quant_blocks(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
                          uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
   dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
   hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, st, w, R, C, ldw, q, ldq, s, qT, ldqT, sT);
+}
+
+void launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                       uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st) {
+  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
+  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, x, R, C, ldx, q, ldq, s, lds, qT, ldqT, sT, ldsT);
 }
 
 void launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t st) {

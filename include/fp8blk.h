@@ -102,6 +102,22 @@ int fp8_quant_1x128(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x
                     float* scales, int64_t ld_s, void* stream);
 
 /*
+ * Both 1x128 orientations of x [rows, cols] from a single read: the outputs of
+ * fp8_quant_1x128 with transpose_out = 0 (q, scales, ld_q, ld_s) and with
+ * transpose_out = 1 (qT, scalesT, ld_qT, ld_sT), bit for bit, for 2 bytes of
+ * HBM read per element instead of 4.  Source: arxiv-wiki Puro-2B summary,
+ * section "접근 방법" item (4) (1-D groups of 128) and paperlayer.ai summary,
+ * appendix C, item "FP8実装pipeline" (X feeds both the forward and the
+ * weight-gradient GEMM, dY both the data- and the weight-gradient GEMM).
+ * Layouts, leading-dimension rules and padding as in fp8_quant_1x128; all
+ * five pointers are required; q and qT 16-byte aligned with ld_q and ld_qT
+ * multiples of 16.
+ */
+int fp8_quant_1x128_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                         uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                         uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT, void* stream);
+
+/*
  * 128x128 block quantiser of a BF16 weight w [rows, cols] (ld_w >= cols).
  * Source: arxiv-wiki Puro-2B summary, section "접근 방법" item (4) (one scale
  * per 128x128 weight block); the transposed copy serves the data-gradient GEMM

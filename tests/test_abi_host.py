@@ -130,3 +130,16 @@ def test_bf16_gemm_validation():
     assert lib.bf16_gemm_nt(P, 64, P, 64, 16, 128, 64, P, 132, 1, None) == 3
     # empty outputs are no-ops
     assert lib.bf16_gemm_nt(None, 0, None, 0, 0, 128, 64, None, 0, 0, None) == 0
+
+
+def test_dual_quantiser_validation():
+    lib = _lib()
+    P = ctypes.c_void_p(16)
+    # missing output, leading dimensions too small, misaligned qT
+    assert lib.fp8_quant_1x128_dual(P, 100, 256, 256, P, 256, P, 100, None, 128, P, 256, None) == 1
+    assert lib.fp8_quant_1x128_dual(P, 100, 256, 256, P, 256, P, 100, P, 112, P, 256, None) == 1
+    assert lib.fp8_quant_1x128_dual(P, 100, 256, 256, P, 256, P, 99, P, 128, P, 256, None) == 1
+    assert lib.fp8_quant_1x128_dual(P, 100, 256, 256, P, 256, P, 100, ctypes.c_void_p(24), 128, P, 256, None) == 3
+    assert lib.fp8_quant_1x128_dual(P, 100, 256, 256, P, 256, P, 100, P, 136, P, 256, None) == 3
+    # empty input is a no-op
+    assert lib.fp8_quant_1x128_dual(None, 0, 256, 256, None, 0, None, 0, None, 0, None, 0, None) == 0

@@ -1,0 +1,85 @@
+"""GPU parity of the Fp8Linear module against the oracle.
+
+One linear of the M=4096 layer shape family at a smaller token count: the
+forward output, the data gradient and the FP32 weight gradient accumulated
+over two micro-batches are checked element by element against the float64
+oracle (same acceptance rule as the GEMM tests), and the FP8 weight cache is
+checked to rebuild exactly when the weight changes.
+"""
+
+import numpy as np
+import pytest
+
+from blockwise_fp8_linear_quant_amd import workloads as W
+from oracle import compare, gemm, quant
+from tests.gpu_util import dev_bf16, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return torch
+
+
+def _oracle_step(xb, wb, dyb):
+    xq, sx = quant.quant_1x128_rows(xb)
+    xqT, sxT = quant.quant_1x128_tokens(xb)
+    wq, sw = quant.quant_128x128(wb)
+    wqT, swT = quant.quant_128x128(np.ascontiguousarray(wb.T))
+    dyq, sdy = quant.quant_1x128_rows(dyb)
+    dyqT, sdyT = quant.quant_1x128_tokens(dyb)
+    return (gemm.fwd(xq, sx, wq, sw), gemm.dgrad(dyq, sdy, wqT, swT), gemm.wgrad(dyqT, sdyT, xqT, sxT))
+
+
+def test_fp8_linear_forward_backward_two_microbatches(torch_mod):
+    torch = torch_mod
+    from blockwise_fp8_linear_quant_amd.linear import Fp8Linear
+    M, K, N = 300, 256, 384          # ragged token count, several tiles
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(2, 1, "qkv", "w"))
+    lin = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous())
+    dw_sum = None
+    bnd_sum = None
+    for mb in range(2):
+        xb = W.normal_bf16((M, K), 1.0, W.seed_for(2, 10 + mb, "qkv", "x"))
+        dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(2, 10 + mb, "qkv", "dy"))
+        x = dev_bf16(xb).contiguous().requires_grad_(True)
+        say("Fp8Linear micro-batch", mb, M, K, N)
+        y = lin(x)
+        y.backward(dev_bf16(dyb).contiguous())
+        torch.cuda.synchronize()
+        (yy, yb), (dxx, dxb), (dww, dwb) = _oracle_step(xb, wb, dyb)
+        ok, rep = compare.check_bf16(host(y.detach()), yy, yb)
+        assert ok, ("forward", mb, rep)
+        ok, rep = compare.check_bf16(host(x.grad), dxx, dxb)
+        assert ok, ("dgrad", mb, rep)
+        dw_sum = dww if dw_sum is None else dw_sum + dww
+        bnd_sum = dwb if bnd_sum is None else bnd_sum + dwb
+    ok, rep = compare.check_fp32(host(lin.weight.main_grad), dw_sum, bnd_sum)
+    assert ok, ("wgrad accumulated", rep)
+    assert lin.weight.grad is None
+    assert lin.weight_quantisations == 1      # one FP8 weight for both micro-batches
+
+
+def test_fp8_linear_weight_cache_follows_updates(torch_mod):
+    torch = torch_mod
+    from blockwise_fp8_linear_quant_amd.linear import Fp8Linear
+    M, K, N = 128, 128, 256
+    wb = W.normal_bf16((N, K), 0.02, 5)
+    lin = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous())
+    xb = W.normal_bf16((M, K), 1.0, 6)
+    x = dev_bf16(xb).contiguous()
+    say("Fp8Linear cache")
+    with torch.no_grad():
+        y0 = lin(x)
+        y1 = lin(x)
+        assert lin.weight_quantisations == 1
+        lin.weight.mul_(2.0)                   # exact in BF16: codes unchanged, scales doubled
+        y2 = lin(x)
+    torch.cuda.synchronize()
+    assert lin.weight_quantisations == 2
+    assert torch.equal(y0, y1)
+    assert torch.equal(y2.float(), (2.0 * y0.float()).to(torch.bfloat16).float())

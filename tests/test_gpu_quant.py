@@ -57,6 +57,20 @@ def check_tokens(B, bits, label):
     assert ok, f"{label}: {n} scales differ"
 
 
+def check_dual(B, bits, label):
+    """Single-read dual quantiser: both orientations bit-exact against the oracle."""
+    say("quant dual", label, bits.shape)
+    M = bits.shape[0]
+    q, s, qT, sT = (host(t) for t in B.fp8_quant_1x128_dual(dev_bf16(bits)))
+    oq, os_ = quant.quant_1x128_rows(bits)
+    oqT, osT = quant.quant_1x128_tokens(bits)
+    assert qT.shape[1] == -(-M // 128) * 128
+    assert np.all(qT[:, M:] == 0), f"{label}: padding bytes not zero"
+    for name, got, ref in (("q", q, oq), ("s", s, os_.T), ("qT", qT[:, :M], oqT), ("sT", sT, osT.T)):
+        ok, n = compare.check_exact(np.ascontiguousarray(got), np.ascontiguousarray(ref))
+        assert ok, f"{label}: {name}: {n} entries differ"
+
+
 def check_blocks(B, bits, label):
     say("quant 128x128", label, bits.shape)
     q, s, qT, sT = B.fp8_quant_128x128(dev_bf16(bits), with_transpose=True)
@@ -78,6 +92,7 @@ def test_small_and_ragged_shapes(B, shape):
     bits = W.normal_bf16(shape, 1.0, W.seed_for(90, shape[0], 0, "x"))
     check_rows(B, bits, "small")
     check_tokens(B, bits, "small")
+    check_dual(B, bits, "small")
     check_blocks(B, bits, "small")
 
 
@@ -111,6 +126,7 @@ def test_special_values(B):
         x[r, 384 + (r % 128)] = (r * 583) & 0x7F7F
     check_rows(B, x, "specials")
     check_tokens(B, x, "specials")
+    check_dual(B, x, "specials")
     check_blocks(B, x, "specials")
     q, s = rows_gpu(B, x)
     assert np.all(q[0] == 0) and s[0, 0] == 0
@@ -126,6 +142,7 @@ def test_every_bf16_magnitude_as_amax(B):
     x[:, 5] = bits >> 3
     x[:, 6] = (bits >> 1) | 0x8000
     check_rows(B, x, "all-amax")
+    check_dual(B, x, "all-amax")
 
 
 def test_config1_tensors(B):
@@ -147,6 +164,8 @@ def test_layer_tensors_M4096(B, lin):
     check_blocks(B, w, f"{lin} W")
     check_rows(B, dy, f"{lin} dY")
     check_tokens(B, dy, f"{lin} dY")
+    check_dual(B, x, f"{lin} X")
+    check_dual(B, dy, f"{lin} dY")
 
 
 def test_outlier_channels_M8192(B):
@@ -156,6 +175,7 @@ def test_outlier_channels_M8192(B):
     assert len(cols) == 20
     check_rows(B, x, "cfg4 X")
     check_tokens(B, x, "cfg4 X")
+    check_dual(B, x, "cfg4 X")
 
 
 def test_stress_ragged_M3000(B):
@@ -166,6 +186,8 @@ def test_stress_ragged_M3000(B):
     check_rows(B, x, "cfg5 X")
     check_tokens(B, x, "cfg5 X")
     check_tokens(B, dy, "cfg5 dY")
+    check_dual(B, x, "cfg5 X")
+    check_dual(B, dy, "cfg5 dY")
     check_blocks(B, w, "cfg5 W")
     _, s = quant.quant_1x128_rows(x)
     assert np.any(s == 0) and np.any((s > 0) & (s < np.finfo(np.float32).tiny))
