@@ -28,7 +28,7 @@ import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/internal.h", "build.py")
-GEMM_KERNEL = "block_gemm_kernel"
+GEMM_KERNEL = "block_gemm_f16_kernel"
 COPY_KERNEL_HINTS = ("copy", "elementwise")
 
 

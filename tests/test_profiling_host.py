@@ -4,13 +4,13 @@ import csv
 
 from blockwise_fp8_linear_quant_amd import profiling
 
-GEMM = ("void fp8blk::(anonymous namespace)::block_gemm_kernel<256, 128, 64, 64, 0, 1, 0, 8, 3>"
+GEMM = ("void fp8blk::(anonymous namespace)::block_gemm_f16_kernel<256, 128, 64, 64, 0, 1, 8, 3>"
         "(unsigned char const*, long, float const*, long)")
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>(int, float*)"
 
 
 def test_short_name_keeps_template_arguments():
-    assert profiling.short_name(GEMM) == "block_gemm_kernel<256, 128, 64, 64, 0, 1, 0, 8, 3>"
+    assert profiling.short_name(GEMM) == "block_gemm_f16_kernel<256, 128, 64, 64, 0, 1, 8, 3>"
     q = "fp8blk::(anonymous namespace)::quant_rows_kernel(unsigned short const*, long)"
     assert profiling.short_name(q) == "quant_rows_kernel"
 
