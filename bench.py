@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--no-fp8-path", action="store_true", help="skip timing the FP8 matrix-core GEMM path")
     ap.add_argument("--no-bf16-baseline", action="store_true", help="skip timing the BF16 GEMMs of the same shapes")
+    ap.add_argument("--no-fusion", action="store_true", help="skip timing the fused producers")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -202,6 +203,55 @@ def bf16_baseline(torch, B, layers, steps, warmup, fp8_gemm_ms, fp8_step_ms, fp8
     return out
 
 
+def producer_fusion(torch, B, layers, steps, warmup):
+    """Fused producers against their unfused form (PyTorch BF16 op, then the dual quantiser).
+
+    SwiGLU: the down projection's input from the gate and up halves of the
+    gate_up forward output [M, 12288]; RMSNorm: the qkv input [M, 2048] with a
+    BF16 gain.  Both write the same codes and scales either way.
+    """
+    import torch.nn.functional as F
+    gu = [L for L in layers if L.name == "gate_up"][0]
+    qkv = [L for L in layers if L.name == "qkv"][0]
+    B.fp8_block_gemm_fwd(gu.xq, gu.sx, gu.wq, gu.sw, y=gu.y)
+    half = gu.n // 2
+    g, u = gu.y[:, :half], gu.y[:, half:]
+    M = g.shape[0]
+    x = qkv.x
+    gamma = (1.0 + 0.1 * torch.randn(x.shape[1], device=x.device)).to(torch.bfloat16)
+    outs_s = B.fp8_quant_1x128_dual(g.contiguous())
+    outs_r = B.fp8_quant_1x128_dual(x)
+    rstd = torch.empty(M, dtype=torch.float32, device=x.device)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def t(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = mk(), mk()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    fused_s = t(lambda: B.fp8_swiglu_quant_1x128_dual(g, u, None, *outs_s))
+    unfused_s = t(lambda: B.fp8_quant_1x128_dual(F.silu(g) * u, *outs_s))
+    fused_r = t(lambda: B.fp8_rmsnorm_quant_1x128_dual(x, gamma, 1e-6, None, rstd, *outs_r))
+    unfused_r = t(lambda: B.fp8_quant_1x128_dual(F.rms_norm(x, (x.shape[1],), gamma, 1e-6), *outs_r))
+    sw_bytes = M * half * (2 + 2 + 1 + 1) + 8 * M * half // 128
+    rn_bytes = M * x.shape[1] * (2 + 2 + 1 + 1) + 8 * M * x.shape[1] // 128 + 4 * M
+    return {"swiglu_to_fp8": {"shape": [M, half], "fused_us": round(fused_s, 2), "unfused_us": round(unfused_s, 2),
+                              "speedup": round(unfused_s / fused_s, 3),
+                              "fused_gbps": round(sw_bytes / (fused_s * 1e-6) / 1e9, 1)},
+            "rmsnorm_to_fp8": {"shape": [M, x.shape[1]], "fused_us": round(fused_r, 2),
+                               "unfused_us": round(unfused_r, 2), "speedup": round(unfused_r / fused_r, 3),
+                               "fused_gbps": round(rn_bytes / (fused_r * 1e-6) / 1e9, 1)},
+            "note": "unfused = PyTorch BF16 op (F.silu(g) * u, F.rms_norm) then fp8_quant_1x128_dual; "
+                    "fused RMSNorm reads x twice (row statistics, then the fused pass)"}
+
+
 def copy_probe(torch, dev, mib):
     """A plain device copy of known size (float32 multiply by one), launched once.
 
@@ -348,6 +398,8 @@ def main():
         "wall_s_timed": round(t_wall, 3),
         "fp8_matrix_core_path": fast,
     }
+    if not args.no_fusion:
+        out["producer_fusion"] = producer_fusion(torch, B, layers, args.steps, args.warmup)
     if not args.no_bf16_baseline:
         out["bf16_baseline"] = bf16_baseline(torch, B, layers, args.steps, args.warmup, gemm_ms, ms_step, f_gemm_ms)
     if not args.no_cpu_baseline:

@@ -16,6 +16,10 @@ _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_s
 SIGNATURES = {
     "fp8_quant_1x128": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp]),
     "fp8_quant_1x128_dual": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "fp8_swiglu_quant_1x128_dual": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                           _vp, _i64, _vp, _i64, _vp]),
+    "fp8_rmsnorm_quant_1x128_dual": (_i32, [_vp, _i64, _vp, ctypes.c_float, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
+                                            _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "fp8_quant_128x128": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp]),
     "fp8_block_gemm_fwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
                                   _vp, _i64, _i32, _vp, _sz, _vp]),

@@ -100,6 +100,60 @@ def fp8_quant_1x128_dual(x, q=None, scales=None, qT=None, scalesT=None):
     return q, scales, qT, scalesT
 
 
+def _dual_outputs(R, C, device, q, scales, qT, scalesT):
+    if q is None:
+        q = _codes(R, C, device)
+    if scales is None:
+        scales = _scales(-(-C // 128), R, device)
+    if qT is None:
+        qT = torch.empty((C, _round_up(R, 128)), dtype=torch.uint8, device=device)
+    if scalesT is None:
+        scalesT = _scales(-(-R // 128), C, device)
+    return q, scales, qT, scalesT
+
+
+def fp8_swiglu_quant_1x128_dual(gate, up, h_out=None, q=None, scales=None, qT=None, scalesT=None):
+    """Both 1x128 orientations of silu(gate) * up, formed in registers.
+
+    Returns (q, scales, qT, scalesT); with h_out (BF16 [R, C]) the fused BF16
+    value is written there too.
+    """
+    _check_2d(gate, torch.bfloat16, "gate")
+    _check_2d(up, torch.bfloat16, "up")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    R, C = gate.shape
+    q, scales, qT, scalesT = _dual_outputs(R, C, gate.device, q, scales, qT, scalesT)
+    st = _lib.load().fp8_swiglu_quant_1x128_dual(
+        _ptr(gate), gate.stride(0), _ptr(up), up.stride(0), R, C, _ptr(q), q.stride(0), _ptr(scales),
+        scales.stride(0), _ptr(qT), qT.stride(0), _ptr(scalesT), scalesT.stride(0),
+        _ptr(h_out), h_out.stride(0) if h_out is not None else 0, _stream(gate))
+    _lib.check(st, "fp8_swiglu_quant_1x128_dual")
+    return q, scales, qT, scalesT
+
+
+def fp8_rmsnorm_quant_1x128_dual(x, gamma, eps=1e-6, y_out=None, rstd=None, q=None, scales=None, qT=None,
+                                 scalesT=None):
+    """Both 1x128 orientations of RMSNorm(x) * gamma, formed in registers.
+
+    Returns (q, scales, qT, scalesT, rstd); with y_out (BF16 [R, C]) the
+    normalised BF16 value is written there too.
+    """
+    _check_2d(x, torch.bfloat16, "x")
+    R, C = x.shape
+    if gamma.dtype != torch.bfloat16 or gamma.dim() != 1 or gamma.shape[0] != C or not gamma.is_contiguous():
+        raise TypeError("gamma must be a contiguous BF16 vector of length cols")
+    q, scales, qT, scalesT = _dual_outputs(R, C, x.device, q, scales, qT, scalesT)
+    if rstd is None:
+        rstd = torch.empty(R, dtype=torch.float32, device=x.device)
+    st = _lib.load().fp8_rmsnorm_quant_1x128_dual(
+        _ptr(x), x.stride(0), _ptr(gamma), float(eps), R, C, _ptr(rstd), _ptr(q), q.stride(0), _ptr(scales),
+        scales.stride(0), _ptr(qT), qT.stride(0), _ptr(scalesT), scalesT.stride(0),
+        _ptr(y_out), y_out.stride(0) if y_out is not None else 0, _stream(x))
+    _lib.check(st, "fp8_rmsnorm_quant_1x128_dual")
+    return q, scales, qT, scalesT, rstd
+
+
 def fp8_quant_128x128(w, with_transpose=False, q=None, scales=None, qT=None, scalesT=None):
     """128x128 block quantisation of BF16 w [rows, cols] -> (q, scales, qT, scalesT)."""
     _check_2d(w, torch.bfloat16, "w")

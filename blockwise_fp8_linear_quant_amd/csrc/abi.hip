@@ -100,6 +100,56 @@ int fp8_quant_1x128_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t
   return finish();
 }
 
+namespace {
+// Output checks shared by the fused dual quantisers (as fp8_quant_1x128_dual).
+int check_dual_outputs(int64_t rows, int64_t cols, const uint8_t* q, int64_t ld_q, const float* scales, int64_t ld_s,
+                       const uint8_t* qT, int64_t ld_qT, const float* scalesT, int64_t ld_sT,
+                       const void* bf16_out, int64_t ld_out) {
+  if (q == nullptr || scales == nullptr || qT == nullptr || scalesT == nullptr) return FP8BLK_INVALID_ARG;
+  const int64_t mpad = (rows + 127) / 128 * 128;
+  if (ld_q < cols || ld_s < rows || ld_qT < mpad || ld_sT < cols) return FP8BLK_INVALID_ARG;
+  if (bf16_out != nullptr && ld_out < cols) return FP8BLK_INVALID_ARG;
+  if (!al16(q) || ld_q % 16 != 0 || !al16(qT) || ld_qT % 16 != 0 || !al4(scales) || !al4(scalesT)) return FP8BLK_MISALIGNED;
+  if (bf16_out != nullptr && (!al16(bf16_out) || ld_out % 8 != 0)) return FP8BLK_MISALIGNED;
+  return FP8BLK_OK;
+}
+}  // namespace
+
+int fp8_swiglu_quant_1x128_dual(const void* gate, int64_t ld_gate, const void* up, int64_t ld_up,
+                                int64_t rows, int64_t cols, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                                uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT,
+                                void* h_bf16, int64_t ld_h, void* stream) {
+  if (rows < 0 || cols < 0) return FP8BLK_INVALID_ARG;
+  if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (gate == nullptr || up == nullptr || ld_gate < cols || ld_up < cols) return FP8BLK_INVALID_ARG;
+  const int rc = check_dual_outputs(rows, cols, q, ld_q, scales, ld_s, qT, ld_qT, scalesT, ld_sT, h_bf16, ld_h);
+  if (rc != FP8BLK_OK) return rc;
+  if (!al16(gate) || !al16(up) || ld_gate % 8 != 0 || ld_up % 8 != 0) return FP8BLK_MISALIGNED;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_swiglu_quant_dual(static_cast<const uint16_t*>(gate), ld_gate, static_cast<const uint16_t*>(up), ld_up,
+                           rows, cols, q, ld_q, scales, ld_s, qT, ld_qT, scalesT, ld_sT,
+                           static_cast<uint16_t*>(h_bf16), ld_h, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+int fp8_rmsnorm_quant_1x128_dual(const void* x, int64_t ld_x, const void* gamma, float eps,
+                                 int64_t rows, int64_t cols, float* rstd,
+                                 uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                                 uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT,
+                                 void* y_bf16, int64_t ld_y, void* stream) {
+  if (rows < 0 || cols < 0 || !(eps >= 0.0f)) return FP8BLK_INVALID_ARG;
+  if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (x == nullptr || gamma == nullptr || rstd == nullptr || ld_x < cols) return FP8BLK_INVALID_ARG;
+  const int rc = check_dual_outputs(rows, cols, q, ld_q, scales, ld_s, qT, ld_qT, scalesT, ld_sT, y_bf16, ld_y);
+  if (rc != FP8BLK_OK) return rc;
+  if (!al16(x) || ld_x % 8 != 0 || !al16(gamma) || !al4(rstd)) return FP8BLK_MISALIGNED;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  launch_rmsnorm_quant_dual(static_cast<const uint16_t*>(x), ld_x, static_cast<const uint16_t*>(gamma), eps,
+                            rows, cols, rstd, q, ld_q, scales, ld_s, qT, ld_qT, scalesT, ld_sT,
+                            static_cast<uint16_t*>(y_bf16), ld_y, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
 int fp8_quant_128x128(const void* w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
                       uint8_t* q, int64_t ld_q, float* scales,
                       uint8_t* qT, int64_t ld_qT, float* scalesT, void* stream) {

@@ -16,6 +16,14 @@ void launch_quant_blocks(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
 void launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                        uint8_t* q, int64_t ldq, float* s, int64_t lds,
                        uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st);
+void launch_swiglu_quant_dual(const uint16_t* g, int64_t ldg, const uint16_t* u, int64_t ldu, int64_t R, int64_t C,
+                              uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                              uint16_t* h, int64_t ldh, hipStream_t st);
+void launch_rmsnorm_quant_dual(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t R, int64_t C,
+                               float* rstd, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                               uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                               uint16_t* y, int64_t ldy, hipStream_t st);
 void launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t st);
 
 // Scale modes of the second GEMM operand.

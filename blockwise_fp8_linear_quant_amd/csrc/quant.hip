@@ -296,10 +296,64 @@ __device__ __forceinline__ uint32_t code4_each(float a, float b, float c, float 
   return enc4(q0, q1, q2, q3);
 }
 
+// Element sources of the dual quantiser: eight BF16 values (bit patterns) of
+// row r starting at column c0, columns >= C as +0.
+struct SrcPlain {   // a BF16 tensor
+  const uint16_t* x;
+  int64_t ldx;
+  __device__ __forceinline__ uint4 load(int64_t r, int64_t c0, int64_t C) const { return load8(x + r * ldx, c0, C); }
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+// SwiGLU of the gate and up halves of the gate_up projection: silu(g) * u
+// evaluated in binary32 (g * (1 / (1 + e^-g)) then times u), rounded once to
+// BF16 -- the down projection's BF16 input, produced in registers.
+struct SrcSwiGLU {
+  const uint16_t* g;
+  int64_t ldg;
+  const uint16_t* u;
+  int64_t ldu;
+  __device__ __forceinline__ uint4 load(int64_t r, int64_t c0, int64_t C) const {
+    const uint4 a = load8(g + r * ldg, c0, C), b = load8(u + r * ldu, c0, C);
+    float h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float gj = elem(a, j);
+      h[j] = (gj / (1.0f + expf(-gj))) * elem(b, j);
+    }
+    return make_uint4(pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]), pack_bf16(h[6], h[7]));
+  }
+};
+
+// RMSNorm output x * rstd(row) * gamma(col) in binary32, rounded once to BF16,
+// with rstd from rmsnorm_rstd_kernel.
+struct SrcRMSNorm {
+  const uint16_t* x;
+  int64_t ldx;
+  const float* rstd;
+  const uint16_t* gamma;
+  __device__ __forceinline__ uint4 load(int64_t r, int64_t c0, int64_t C) const {
+    const uint4 a = load8(x + r * ldx, c0, C), w = load8(gamma, c0, C);
+    const float rs = rstd[r];
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = (elem(a, j) * rs) * elem(w, j);
+    return make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
+  }
+};
+
+// The dual quantiser over any element source.  `hout` (optional, BF16
+// [R, ld_h]) receives the source values themselves -- for a fused producer,
+// the BF16 tensor it would otherwise have written.
+template <class Src>
 __global__ __launch_bounds__(256) void quant_dual_kernel(
-    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
+    Src src, int64_t R, int64_t C,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
-    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT) {
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
+    uint16_t* __restrict__ hout, int64_t ldh) {
   __shared__ float cred[4][128];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t br = blockIdx.y, bc = blockIdx.x;
@@ -310,7 +364,23 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t r = r0 + i;
-    v[i] = (r < R && c0 < C) ? load8(x + r * ldx, c0, C) : make_uint4(0, 0, 0, 0);
+    v[i] = (r < R && c0 < C) ? src.load(r, c0, C) : make_uint4(0, 0, 0, 0);
+  }
+  if (hout != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + i;
+      if (r < R && c0 < C) {
+        uint16_t* p = hout + r * ldh + c0;
+        if (c0 + 8 <= C) {
+          *reinterpret_cast<uint4*>(p) = v[i];
+        } else {
+          const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          for (int j = 0; j < 8; ++j)
+            if (c0 + j < C) p[j] = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+        }
+      }
+    }
   }
   // Column maxima of this thread's 8 columns over its 8 rows, then over the
   // 4 row blocks of the wave (lanes 16 and 32 apart), then over the waves.
@@ -387,6 +457,29 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   }
 }
 
+// RMSNorm statistics: rstd[r] = 1 / sqrt(mean_c x[r, c]^2 + eps) in binary32,
+// one wave per row (squares are exact in binary32; the sum is accumulated per
+// lane over 8-element chunks and then across the wave).
+__global__ __launch_bounds__(256) void rmsnorm_rstd_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                           int64_t ldx, float eps, float* __restrict__ rstd) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const uint16_t* row = x + r * ldx;
+  float acc = 0.0f;
+  for (int64_t c0 = (int64_t)lane * 8; c0 < C; c0 += 512) {
+    const uint4 v = load8(row, c0, C);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e = elem(v, j);
+      acc = fmaf(e, e, acc);
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (lane == 0) rstd[r] = 1.0f / sqrtf(acc / (float)C + eps);
+}
+
 }  // namespace
 
 void launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
@@ -412,7 +505,27 @@ void launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                        uint8_t* q, int64_t ldq, float* s, int64_t lds,
                        uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st) {
   dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
-  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, x, R, C, ldx, q, ldq, s, lds, qT, ldqT, sT, ldsT);
+  hipLaunchKernelGGL(quant_dual_kernel<SrcPlain>, grid, dim3(256), 0, st, SrcPlain{x, ldx}, R, C, q, ldq, s, lds,
+                     qT, ldqT, sT, ldsT, (uint16_t*)nullptr, (int64_t)0);
+}
+
+void launch_swiglu_quant_dual(const uint16_t* g, int64_t ldg, const uint16_t* u, int64_t ldu, int64_t R, int64_t C,
+                              uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                              uint16_t* h, int64_t ldh, hipStream_t st) {
+  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
+  hipLaunchKernelGGL(quant_dual_kernel<SrcSwiGLU>, grid, dim3(256), 0, st, SrcSwiGLU{g, ldg, u, ldu}, R, C,
+                     q, ldq, s, lds, qT, ldqT, sT, ldsT, h, ldh);
+}
+
+void launch_rmsnorm_quant_dual(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t R, int64_t C,
+                               float* rstd, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                               uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                               uint16_t* y, int64_t ldy, hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_rstd_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, x, R, C, ldx, eps, rstd);
+  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
+  hipLaunchKernelGGL(quant_dual_kernel<SrcRMSNorm>, grid, dim3(256), 0, st, SrcRMSNorm{x, ldx, rstd, gamma}, R, C,
+                     q, ldq, s, lds, qT, ldqT, sT, ldsT, y, ldy);
 }
 
 void launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t st) {

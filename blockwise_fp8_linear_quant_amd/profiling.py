@@ -27,13 +27,13 @@ import os
 import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCES = ("csrc/gemm.hip", "csrc/internal.h", "build.py")
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/fp8_codec.h", "build.py")
 GEMM_KERNEL = "block_gemm_f16_kernel"
 COPY_KERNEL_HINTS = ("copy", "elementwise")
 
 
 def source_digest(files=GEMM_SOURCES):
-    """sha256 over the GEMM kernel's source files and the build script (its flags)."""
+    """sha256 over the GEMM kernel source, the codec header it includes and the build script (its flags)."""
     h = hashlib.sha256()
     for rel in files:
         with open(os.path.join(_HERE, rel), "rb") as f:

@@ -118,6 +118,43 @@ int fp8_quant_1x128_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t
                          uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT, void* stream);
 
 /*
+ * Producer fusion: SwiGLU straight into both 1x128 orientations.  The BF16
+ * value h = silu(g) * u (binary32: g / (1 + e^-g) * u, rounded once to BF16 to
+ * nearest even) of the gate g and up u halves of the gate_up projection is
+ * formed in registers and quantised exactly as fp8_quant_1x128_dual would
+ * quantise a BF16 tensor holding it -- the down projection's operands for the
+ * forward (q) and weight-gradient (qT) GEMMs, without writing h.  Source:
+ * paperlayer.ai Puro-2B summary, appendix C, item "FP8実装pipeline" (the BF16
+ * hidden flow feeding the FP8 linear GEMMs; the model is the Qwen3-1.7B
+ * architecture, arxiv-wiki summary, "접근 방법" item (1), whose MLP is SwiGLU).
+ * gate [rows, ld_gate >= cols], up [rows, ld_up >= cols] BF16, 16-byte aligned,
+ * ld multiples of 8; outputs as in fp8_quant_1x128_dual; h_bf16 (nullable)
+ * [rows, ld_h >= cols] receives h itself (16-byte aligned, ld_h % 8 == 0).
+ */
+int fp8_swiglu_quant_1x128_dual(const void* gate, int64_t ld_gate, const void* up, int64_t ld_up,
+                                int64_t rows, int64_t cols, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                                uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT,
+                                void* h_bf16, int64_t ld_h, void* stream);
+
+/*
+ * Producer fusion: RMSNorm straight into both 1x128 orientations.  Per row,
+ * rstd = 1 / sqrt(mean(x^2) + eps) (binary32, written to rstd[rows] for the
+ * backward pass); y = x * rstd * gamma in binary32, rounded once to BF16, is
+ * formed in registers and quantised as fp8_quant_1x128_dual would quantise a
+ * BF16 tensor holding it (the qkv and gate_up inputs), without writing y.
+ * Source: paperlayer.ai Puro-2B summary, appendix C, item "FP8実装pipeline"
+ * (normalisation in the BF16 flow ahead of the FP8 GEMMs).  x [rows, ld_x >=
+ * cols] BF16 and gamma [cols] BF16, 16-byte aligned, ld_x % 8 == 0; eps >= 0;
+ * rstd 4-byte aligned; outputs as in fp8_quant_1x128_dual; y_bf16 (nullable)
+ * receives y.  Two launches on the stream: row statistics, then the fused pass.
+ */
+int fp8_rmsnorm_quant_1x128_dual(const void* x, int64_t ld_x, const void* gamma, float eps,
+                                 int64_t rows, int64_t cols, float* rstd,
+                                 uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s,
+                                 uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT,
+                                 void* y_bf16, int64_t ld_y, void* stream);
+
+/*
  * 128x128 block quantiser of a BF16 weight w [rows, cols] (ld_w >= cols).
  * Source: arxiv-wiki Puro-2B summary, section "접근 방법" item (4) (one scale
  * per 128x128 weight block); the transposed copy serves the data-gradient GEMM

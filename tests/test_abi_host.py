@@ -143,3 +143,24 @@ def test_dual_quantiser_validation():
     assert lib.fp8_quant_1x128_dual(P, 100, 256, 256, P, 256, P, 100, P, 136, P, 256, None) == 3
     # empty input is a no-op
     assert lib.fp8_quant_1x128_dual(None, 0, 256, 256, None, 0, None, 0, None, 0, None, 0, None) == 0
+
+
+def test_fused_producer_validation():
+    lib = _lib()
+    P = ctypes.c_void_p(16)
+    # SwiGLU: missing up, ld too small, misaligned optional BF16 output
+    assert lib.fp8_swiglu_quant_1x128_dual(P, 256, None, 256, 100, 256, P, 256, P, 100, P, 128, P, 256,
+                                           None, 0, None) == 1
+    assert lib.fp8_swiglu_quant_1x128_dual(P, 128, P, 256, 100, 256, P, 256, P, 100, P, 128, P, 256,
+                                           None, 0, None) == 1
+    assert lib.fp8_swiglu_quant_1x128_dual(P, 256, P, 256, 100, 256, P, 256, P, 100, P, 128, P, 256,
+                                           ctypes.c_void_p(20), 256, None) == 3
+    # RMSNorm: negative eps, missing rstd, misaligned gamma
+    assert lib.fp8_rmsnorm_quant_1x128_dual(P, 256, P, -1.0, 100, 256, P, P, 256, P, 100, P, 128, P, 256,
+                                            None, 0, None) == 1
+    assert lib.fp8_rmsnorm_quant_1x128_dual(P, 256, P, 1e-6, 100, 256, None, P, 256, P, 100, P, 128, P, 256,
+                                            None, 0, None) == 1
+    assert lib.fp8_rmsnorm_quant_1x128_dual(P, 256, ctypes.c_void_p(18), 1e-6, 100, 256, P, P, 256, P, 100,
+                                            P, 128, P, 256, None, 0, None) == 3
+    assert lib.fp8_rmsnorm_quant_1x128_dual(None, 0, None, 1e-6, 0, 256, None, None, 0, None, 0, None, 0, None, 0,
+                                            None, 0, None) == 0
