@@ -66,6 +66,45 @@ FP8BLK_HD GroupQ group_setup(float amax) {
   return g;
 }
 
+// The same constants from a 128-entry table, for group maxima that are BF16
+// values (low 16 bits zero).  For a normal BF16 amax = (128 + m) * 2^(e - 134)
+// (e the biased exponent, m the 7 stored mantissa bits),
+//     amax / 448 = ((128 + m) / 7) * 2^(e - 140),
+// and scaling by a power of two commutes with rounding while the result stays
+// normal, so fl32(amax / 448) = T(m) * 2^(e - 140) with T(m) = fl32((128+m)/7)
+// in [18.28, 36.43].  The table holds T(m) normalised to [1, 2) (by 2^-4, or
+// 2^-5 from m = 96 on, where (128 + m) / 7 reaches 32 exactly) and its
+// correctly rounded reciprocal; the stored scale is rebuilt with one ldexp.
+// Maxima with e < 10 (scales at or below the binary32 normal range), zero,
+// and non-finite values take group_setup itself.  Equal to group_setup on
+// every BF16 amax (checked exhaustively on the host).
+struct SetupEntry {
+  float s_n;
+  float r_n;
+};
+
+FP8BLK_HD SetupEntry setup_entry(int m) {
+  const float t = (float)(128 + m) / 7.0f;
+  SetupEntry e;
+  e.s_n = ldexpf(t, m >= 96 ? -5 : -4);
+  e.r_n = 1.0f / e.s_n;
+  return e;
+}
+
+FP8BLK_HD GroupQ group_setup_bf16(float amax, const SetupEntry* tab) {
+  const uint32_t b = f32_bits(amax);
+  const int e = (int)(b >> 23);
+  if (e < 10 || e > 254) return group_setup(amax);
+  const int m = (int)((b >> 16) & 0x7fu);
+  const SetupEntry t = tab[m];
+  GroupQ g;
+  g.k = 140 - e - (m >= 96 ? 5 : 4);
+  g.s_n = t.s_n;
+  g.r_n = t.r_n;
+  g.s = ldexpf(t.s_n, -g.k);
+  return g;
+}
+
 // fl32(x / s) for every x whose quotient can reach a non-zero code; tiny
 // quotients (< 2^-12) come out tiny with the right sign, which encodes the same.
 FP8BLK_HD float group_quotient(float x, const GroupQ& g) {

@@ -355,7 +355,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
     uint16_t* __restrict__ hout, int64_t ldh) {
   __shared__ float cred[4][128];
+  __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t < 128) stab[t] = setup_entry(t);
   const int64_t br = blockIdx.y, bc = blockIdx.x;
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   // Row-wise codes and scales.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const GroupQ gq = group_setup(rm[i]);
+    const GroupQ gq = group_setup_bf16(rm[i], stab);
     const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
     const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gq);
     const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gq);
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   // byte transposes into words of 4 tokens each.
   GroupQ gc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) gc[j] = group_setup(cm[j]);
+  for (int j = 0; j < 8; ++j) gc[j] = group_setup_bf16(cm[j], stab);
   uint32_t rw[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

@@ -45,6 +45,26 @@ extern "C" int codec_quotient_scan(uint32_t amax_lo, uint32_t amax_hi, uint64_t*
   return (int)(bad > 0x7fffffff ? 0x7fffffff : bad);
 }
 
+// Table-driven group setup against group_setup for every BF16 magnitude:
+// returns the number of maxima whose four constants differ in any bit.
+extern "C" int codec_setup_table_scan(void) {
+  fp8blk::SetupEntry tab[128];
+  for (int m = 0; m < 128; ++m) tab[m] = fp8blk::setup_entry(m);
+  int bad = 0;
+  for (uint32_t ab = 0; ab < 0x7f80; ++ab) {
+    const float amax = fp8blk::bf16_to_f32(ab);
+    const fp8blk::GroupQ a = fp8blk::group_setup(amax), b = fp8blk::group_setup_bf16(amax, tab);
+    const bool same = fp8blk::f32_bits(a.s) == fp8blk::f32_bits(b.s) && a.k == b.k &&
+                      (a.s == 0.0f || (fp8blk::f32_bits(a.s_n) == fp8blk::f32_bits(b.s_n) &&
+                                       fp8blk::f32_bits(a.r_n) == fp8blk::f32_bits(b.r_n)));
+    if (!same) {
+      if (bad < 10) std::printf("SETUP MISMATCH amax=%#x s %a %a k %d %d\n", ab, a.s, b.s, a.k, b.k);
+      ++bad;
+    }
+  }
+  return bad;
+}
+
 int main() {
   uint64_t n = 0;
   int bad = codec_quotient_scan(1, 0x7f80, &n);

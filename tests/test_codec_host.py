@@ -6,6 +6,8 @@
    whenever it is >= 2^-12.
 2. The device E4M3 encoder equals the oracle's encoder on every positive
    binary32 in [2^-12, 2^10) and on a random sample of all bit patterns.
+3. The table-driven group setup the kernels use for BF16 group maxima gives
+   the same four constants as the direct one for every BF16 magnitude.
 """
 
 import ctypes
@@ -35,7 +37,12 @@ def codec_lib(tmp_path_factory):
     lib.codec_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
     lib.codec_quotient_scan.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint64)]
     lib.codec_quotient_scan.restype = ctypes.c_int
+    lib.codec_setup_table_scan.restype = ctypes.c_int
     return lib
+
+
+def test_table_setup_equals_direct_setup_for_every_bf16_amax(codec_lib):
+    assert codec_lib.codec_setup_table_scan() == 0
 
 
 def test_exact_quotient_equals_ieee_division_for_all_bf16_pairs(codec_lib):
