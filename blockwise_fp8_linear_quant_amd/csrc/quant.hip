@@ -70,11 +70,11 @@ __device__ __forceinline__ uint32_t code4(float a, float b, float c, float d, co
 }
 
 // Any binary32 -> E4M3 code: hardware below 464, saturation at and above it
-// (infinities included); NaN keeps the hardware's NaN code.
+// (infinities included), and S.1111.111 (0x7F with the sign) for NaN.
 __device__ __forceinline__ uint32_t encode_any(float x) {
   const uint32_t u = f32_bits(x), a = u & 0x7fffffffu;
   uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xffu;
-  if (a >= 0x43e80000u && a <= 0x7f800000u) c = 0x7eu | ((u >> 24) & 0x80u);
+  if (a >= 0x43e80000u) c = (a > 0x7f800000u ? 0x7fu : 0x7eu) | ((u >> 24) & 0x80u);
   return c;
 }
 

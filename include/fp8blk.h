@@ -260,9 +260,10 @@ size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K);
 
 /*
  * The library's binary32 -> E4M3 encoder applied elementwise: q[i] = E4M3(x[i])
- * with round-to-nearest-even, saturation at +-448 and the sign kept (OCP E4M3,
- * the format named in the arxiv-wiki Puro-2B summary, "접근 방법" item (4)).
- * Exposed so the device encoder can be checked on every binary32 input.
+ * with round-to-nearest-even, saturation at +-448 (infinities included), the
+ * sign kept, and NaN -> 0x7F with its sign (OCP E4M3, the format named in the
+ * arxiv-wiki Puro-2B summary, "접근 방법" item (4)).  Exposed so the device
+ * encoder can be checked on every binary32 input.
  * x: n floats, q: n bytes, both device pointers (no alignment requirement).
  */
 int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, void* stream);

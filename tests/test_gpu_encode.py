@@ -1,12 +1,14 @@
 """GPU parity of the device E4M3 encoder (through fp8_e4m3_encode) against the
-oracle, on every binary32 of magnitude in [2^-12, 2^10) (both signs) and on
-random bit patterns.  The encoder shares the hardware conversion the
+oracle: on every binary32 of magnitude in [2^-12, 2^10) (both signs) against
+the oracle's encoder itself, on random bit patterns, and on all 2^32 bit
+patterns against the oracle's decision boundaries (tests/encode_rule.py).  The encoder shares the hardware conversion the
 quantisers use, so this also pins that conversion."""
 
 import numpy as np
 import pytest
 
 from oracle import e4m3
+from tests.encode_rule import decision_midpoints, expected_codes_torch
 from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu
@@ -40,3 +42,19 @@ def test_device_encoder_random_and_specials():
     v = np.concatenate([v, sp])
     got = B.fp8_e4m3_encode(torch.from_numpy(v).cuda()).cpu().numpy()
     assert np.array_equal(got, e4m3.encode(v))
+
+
+def test_device_encoder_all_binary32():
+    """Every one of the 2^32 binary32 bit patterns through the device encoder."""
+    import torch
+    from blockwise_fp8_linear_quant_amd import binding as B
+    mids = torch.from_numpy(decision_midpoints()).cuda()
+    chunk = 1 << 28
+    for start in range(0, 1 << 32, chunk):
+        say("encode all-binary32 chunk", hex(start))
+        b64 = torch.arange(start, start + chunk, dtype=torch.int64, device="cuda")
+        bits = torch.where(b64 >= 2 ** 31, b64 - 2 ** 32, b64).to(torch.int32)   # the same 32 bits, signed
+        got = B.fp8_e4m3_encode(bits.view(torch.float32)).to(torch.int64)
+        want = expected_codes_torch(torch, bits, mids)
+        bad = int((got != want).sum())
+        assert bad == 0, (hex(start), bad)

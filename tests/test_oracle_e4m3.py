@@ -135,3 +135,19 @@ def test_ties_and_saturation_closed_forms():
     assert np.all(e4m3.encode(big) == 0x7E)
     assert np.all(e4m3.encode(-big) == 0xFE)
     assert np.all(e4m3.encode(np.array([np.nan], dtype=np.float32)) & 0x7F == 0x7F)
+
+
+def test_decision_rule_matches_the_encoder():
+    """The boundary rule used for the all-binary32 GPU scan reproduces encode()."""
+    import torch
+    from tests.encode_rule import decision_midpoints, expected_codes_torch
+    rng = np.random.default_rng(77)
+    bits = rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    dense = np.arange(int(np.float32(2.0 ** -11).view(np.uint32)), int(np.float32(500.0).view(np.uint32)), 97,
+                      dtype=np.uint32)
+    specials = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 1, 0x80000001],
+                        dtype=np.uint32)
+    bits = np.concatenate([bits, dense, dense | np.uint32(0x80000000), specials])
+    mids = torch.from_numpy(decision_midpoints())
+    got = expected_codes_torch(torch, torch.from_numpy(bits.view(np.int32)), mids)
+    assert np.array_equal(got.numpy().astype(np.uint8), e4m3.encode(bits.view(np.float32)))
