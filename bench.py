@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-fp8-path", action="store_true", help="skip timing the FP8 matrix-core GEMM path")
     ap.add_argument("--no-bf16-baseline", action="store_true", help="skip timing the BF16 GEMMs of the same shapes")
     ap.add_argument("--no-fusion", action="store_true", help="skip timing the fused producers")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 28-layer M=8192 sweep")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -54,13 +55,14 @@ def parse():
 class LayerBuffers:
     """Device inputs and preallocated outputs for one linear of the layer."""
 
-    def __init__(self, torch, B, W, name, k, n, M, dev):
+    def __init__(self, torch, B, W, name, k, n, M, dev, cfg=2, layer=0, outliers=False):
         import numpy as np
         self.name, self.k, self.n, self.M = name, k, n, M
-        cfg = 2
-        self.xb = W.normal_bf16((M, k), 1.0, W.seed_for(cfg, 0, name, "x"))
-        self.wb = W.normal_bf16((n, k), 0.02, W.seed_for(cfg, 0, name, "w"))
-        self.dyb = W.normal_bf16((M, n), 1e-3, W.seed_for(cfg, 0, name, "dy"))
+        self.xb = W.normal_bf16((M, k), 1.0, W.seed_for(cfg, layer, name, "x"))
+        if outliers:   # configuration 4: round(1% of K) input channels scaled by 32
+            self.xb, _ = W.with_outlier_channels(self.xb, 0.01, 32, W.seed_for(cfg, layer, name, "x").spawn(1)[0])
+        self.wb = W.normal_bf16((n, k), 0.02, W.seed_for(cfg, layer, name, "w"))
+        self.dyb = W.normal_bf16((M, n), 1e-3, W.seed_for(cfg, layer, name, "dy"))
         to = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         self.x, self.w, self.dy = to(self.xb), to(self.wb), to(self.dyb)
         # Outputs (allocated once, reused every step).
@@ -200,6 +202,43 @@ def bf16_baseline(torch, B, layers, steps, warmup, fp8_gemm_ms, fp8_step_ms, fp8
            "note": "BF16 GEMMs of the same 12 shapes; the FP8 step includes its quantisers"}
     if fp8_mc_gemm_ms is not None:
         out["speedup_fp8_matrix_core_gemms_vs_hipblaslt"] = round(blas_ms / fp8_mc_gemm_ms, 3)
+    return out
+
+
+def layer_sweep(torch, B, W, dev, n_layers=28, M=8192, sweeps=3):
+    """Configuration 4: the whole hot path of 28 decoder layers at 8192 tokens.
+
+    Each layer quantises X (both orientations), W (with its transposed copy) and
+    dY (both orientations) of its four linears and runs their forward, dgrad and
+    wgrad GEMMs.  Inputs have 1% outlier channels.  Two seeded layer sets
+    (layers 0 and 1) are generated and alternate over the 28 layers, which keeps
+    the input generation to seconds; the kernels' work does not depend on which
+    set a layer reads.
+    """
+    sets = [[LayerBuffers(torch, B, W, n, k, nout, M, dev, cfg=4, layer=l, outliers=True) for n, k, nout in W.LINEARS]
+            for l in (0, 1)]
+
+    def sweep():
+        for layer in range(n_layers):
+            for L in sets[layer % 2]:
+                L.quantise(B)
+                L.gemms(B)
+
+    sweep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(sweeps):
+        sweep()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / sweeps
+    flops = n_layers * sum(L.flops() for L in sets[0])
+    out = {"layers": n_layers, "tokens": M, "ms_per_sweep": round(ms, 3), "gemm_tflop_per_sweep": round(flops / 1e12, 3),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "inputs": "two seeded layer sets (1% outlier channels x32) alternating over the layers"}
+    del sets
+    torch.cuda.empty_cache()
     return out
 
 
@@ -398,6 +437,8 @@ def main():
         "wall_s_timed": round(t_wall, 3),
         "fp8_matrix_core_path": fast,
     }
+    if not args.no_sweep:
+        out["cfg4_sweep"] = layer_sweep(torch, B, W, dev)
     if not args.no_fusion:
         out["producer_fusion"] = producer_fusion(torch, B, layers, args.steps, args.warmup)
     if not args.no_bf16_baseline:
