@@ -1,0 +1,105 @@
+"""Pins for the decoder-layer reference (oracle/layer.py), CPU only.
+
+Closed forms and special cases that a wiring slip would break:
+* RoPE: identity at position 0; at position p the pair (i, i+64) turns by
+  p * 1e6^(-i/64) radians (checked against math.cos/sin at p = 1, 3);
+* attention: the first query sees only the first key (its output is that
+  value row); equal keys give the running mean of the values; query heads
+  2h and 2h+1 read key/value head h (a distinct value per head shows it);
+* RMSNorm of a constant row is +-1; silu(gate) (up = 1) equals the pinned
+  fused reference, and the layer rounds it to BF16 before multiplying by up;
+* the whole layer with zero output projections is the identity (residuals),
+  and with a zero down projection it is x + o(attention) alone.
+"""
+
+import math
+
+import numpy as np
+
+from oracle import fused, gemm
+from oracle import layer as L
+
+
+def bf16_bits(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_rope_position_zero_and_rotation_angle():
+    rng = np.random.default_rng(1)
+    t = gemm.round_to_bf16(rng.standard_normal((1, 4, 128)))
+    out, _ = L.rope(t)
+    assert np.array_equal(out[0, 0], t[0, 0])
+    for p in (1, 3):
+        for i in (0, 5, 63):
+            ang = p * L.ROPE_THETA ** (-i / 64)
+            a, b = t[0, p, i], t[0, p, i + 64]
+            want_a = a * math.cos(ang) - b * math.sin(ang)
+            want_b = b * math.cos(ang) + a * math.sin(ang)
+            assert out[0, p, i] == gemm.round_to_bf16(want_a)
+            assert out[0, p, i + 64] == gemm.round_to_bf16(want_b)
+
+
+def test_attention_first_query_and_equal_keys():
+    rng = np.random.default_rng(2)
+    s = 6
+    q = rng.standard_normal((16, s, 128))
+    k = np.ones((8, s, 128))
+    v = gemm.round_to_bf16(rng.standard_normal((8, s, 128)))
+    out, _ = L.attention(q, k, v)
+    out = out.reshape(s, 16, 128)
+    for h in range(16):
+        assert np.array_equal(out[0, h], v[h // 2, 0])
+        for i in range(s):
+            np.testing.assert_allclose(out[i, h], gemm.round_to_bf16(v[h // 2, :i + 1].mean(axis=0)),
+                                       rtol=2.0 ** -7, atol=1e-12)
+
+
+def test_attention_head_sharing():
+    s = 3
+    q = np.zeros((16, s, 128))
+    k = np.zeros((8, s, 128))
+    v = np.zeros((8, s, 128))
+    for h in range(8):
+        v[h, :, :] = h + 1.0
+    out, _ = L.attention(q, k, v)
+    out = out.reshape(s, 16, 128)
+    for h in range(16):
+        assert np.all(out[:, h] == h // 2 + 1.0)
+
+
+def test_rms_norm_constant_rows_and_swiglu():
+    x = np.array([[3.0] * 64, [-0.25] * 64])
+    y = L.rms_norm(x)
+    assert np.allclose(y[0], 1.0, atol=2.0 ** -8) and np.allclose(y[1], -1.0, atol=2.0 ** -8)
+    rng = np.random.default_rng(4)
+    g = bf16_bits(rng.standard_normal((2, L.INTER)).astype(np.float32))
+    one = bf16_bits(np.ones((2, L.INTER), dtype=np.float32))
+    gu = np.concatenate([L.bf16_values(g), L.bf16_values(one)], axis=1)
+    silu = L.swiglu(gu)           # up = 1: silu(gate) rounded once
+    assert np.array_equal(silu, L.bf16_values(fused.swiglu_bf16(g, one)))
+    u = bf16_bits(rng.standard_normal((2, L.INTER)).astype(np.float32))
+    gu = np.concatenate([L.bf16_values(g), L.bf16_values(u)], axis=1)
+    assert np.array_equal(L.swiglu(gu), gemm.round_to_bf16(silu * L.bf16_values(u)))
+
+
+def _weights(rng, zero=()):
+    shapes = [(4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144)]
+    out = []
+    for i, sh in enumerate(shapes):
+        w = np.zeros(sh, dtype=np.float32) if i in zero else rng.standard_normal(sh).astype(np.float32) * 0.02
+        out.append(bf16_bits(w))
+    return out
+
+
+def test_forward_residual_paths():
+    rng = np.random.default_rng(5)
+    x = bf16_bits(rng.standard_normal((8, 2048)).astype(np.float32) * 0.5)
+    xv = L.bf16_values(x)
+    w = _weights(rng, zero=(1, 3))
+    assert np.array_equal(L.forward(x, *w), xv)
+    w = _weights(rng, zero=(3,))
+    qkv = gemm.round_to_bf16(L.fp8_linear(L.rms_norm(xv), w[0])[0])
+    q, k, v = L.split_heads(qkv)
+    a = L.attention(L.rope(L.rms_norm(q))[0], L.rope(L.rms_norm(k))[0], v)[0]
+    want = gemm.round_to_bf16(xv + gemm.round_to_bf16(L.fp8_linear(a, w[1])[0]))
+    assert np.array_equal(L.forward(x, *w), want)
