@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-bf16-baseline", action="store_true", help="skip timing the BF16 GEMMs of the same shapes")
     ap.add_argument("--no-fusion", action="store_true", help="skip timing the fused producers")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 28-layer M=8192 sweep")
+    ap.add_argument("--no-layer", action="store_true", help="skip the whole decoder layer fwd+bwd")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -291,6 +292,83 @@ def producer_fusion(torch, B, layers, steps, warmup):
                     "fused RMSNorm reads x twice (row statistics, then the fused pass)"}
 
 
+def decoder_layer(torch, steps, warmup, batch=2, seq=4096):
+    """Forward + backward of one whole decoder layer (hidden 2048, 16 query and 8
+    key/value heads of 128, intermediate 6144) at 2 x 4096 tokens, with the four
+    linears as Fp8Linear and, for comparison, as BF16 nn.Linear.
+
+    A second, hooked pass of the FP8 layer brackets each linear's forward and
+    backward (quantisers, GEMMs, main_grad accumulation) with events on the
+    current stream, which gives the linears' share of the layer's time.
+    """
+    from blockwise_fp8_linear_quant_amd.layer import DecoderLayer
+    g = torch.Generator().manual_seed(17)
+    x0 = (torch.randn((batch, seq, 2048), generator=g) * 0.5).to(torch.bfloat16).cuda()
+    dy = (torch.randn((batch, seq, 2048), generator=g) * 1e-3).to(torch.bfloat16).cuda()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def run(lay, n):
+        for _ in range(n):
+            x = x0.detach().requires_grad_(True)
+            lay.zero_grad(set_to_none=True)
+            lay(x).backward(dy)
+
+    def t(lay):
+        run(lay, warmup)
+        torch.cuda.synchronize()
+        e0, e1 = mk(), mk()
+        e0.record()
+        run(lay, steps)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    res = {}
+    for fp8 in (True, False):
+        lay = DecoderLayer(fp8=fp8, seed=5)
+        res[fp8] = t(lay)
+        if fp8:
+            spans = []
+
+            def pre(mod, *a):
+                e = mk()
+                e.record()
+                spans.append([e, None])
+
+            def post(mod, *a):
+                e = mk()
+                e.record()
+                spans[-1][1] = e
+            hooks = []
+            for lin in lay.linears():
+                hooks += [lin.register_forward_pre_hook(pre), lin.register_forward_hook(post),
+                          lin.register_full_backward_pre_hook(pre), lin.register_full_backward_hook(post)]
+            run(lay, warmup)
+            torch.cuda.synchronize()
+            spans.clear()
+            e0, e1 = mk(), mk()
+            e0.record()
+            run(lay, steps)
+            e1.record()
+            torch.cuda.synchronize()
+            hooked_ms = e0.elapsed_time(e1) / steps
+            lin_ms = sum(a.elapsed_time(b) for a, b in spans) / steps
+            for h in hooks:
+                h.remove()
+        del lay
+        torch.cuda.empty_cache()
+    tokens = batch * seq
+    lin_flops = 3 * 2 * tokens * (2048 * (4096 + 2048 + 12288) + 6144 * 2048)
+    attn_flops = 3.5 * 4 * batch * seq * seq * 16 * 128 / 2
+    return {"tokens": tokens, "batch": batch, "seq": seq,
+            "fp8_layer_ms": round(res[True], 3), "bf16_layer_ms": round(res[False], 3),
+            "speedup_fp8_vs_bf16_layer": round(res[False] / res[True], 3),
+            "fp8_linears_ms": round(lin_ms, 3), "fp8_linears_share_of_layer_time": round(lin_ms / hooked_ms, 3),
+            "linears_share_of_layer_flops": round(lin_flops / (lin_flops + attn_flops), 3),
+            "note": "fwd+bwd; attention is PyTorch SDPA (causal, GQA) in BF16, norms/RoPE/SwiGLU PyTorch BF16; "
+                    "linears' time from events around each Fp8Linear forward and backward (hooked pass)"}
+
+
 def copy_probe(torch, dev, mib):
     """A plain device copy of known size (float32 multiply by one), launched once.
 
@@ -441,6 +519,8 @@ def main():
         out["cfg4_sweep"] = layer_sweep(torch, B, W, dev)
     if not args.no_fusion:
         out["producer_fusion"] = producer_fusion(torch, B, layers, args.steps, args.warmup)
+    if not args.no_layer:
+        out["decoder_layer"] = decoder_layer(torch, args.steps, args.warmup)
     if not args.no_bf16_baseline:
         out["bf16_baseline"] = bf16_baseline(torch, B, layers, args.steps, args.warmup, gemm_ms, ms_step, f_gemm_ms)
     if not args.no_cpu_baseline:
