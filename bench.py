@@ -295,11 +295,12 @@ def producer_fusion(torch, B, layers, steps, warmup):
 def decoder_layer(torch, steps, warmup, batch=2, seq=4096):
     """Forward + backward of one whole decoder layer (hidden 2048, 16 query and 8
     key/value heads of 128, intermediate 6144) at 2 x 4096 tokens, with the four
-    linears as Fp8Linear and, for comparison, as BF16 nn.Linear.
+    linears as Fp8Linear (exact block products, and the FP8 matrix
+    instructions) and, for comparison, as BF16 nn.Linear (hipBLASLt).
 
-    A second, hooked pass of the FP8 layer brackets each linear's forward and
-    backward (quantisers, GEMMs, main_grad accumulation) with events on the
-    current stream, which gives the linears' share of the layer's time.
+    A second, hooked pass of each layer brackets each linear's forward and
+    backward (for FP8: quantisers, GEMMs, main_grad accumulation) with events on
+    the current stream, which gives the linears' share of the layer's time.
     """
     from blockwise_fp8_linear_quant_amd.layer import DecoderLayer
     g = torch.Generator().manual_seed(17)
@@ -323,50 +324,57 @@ def decoder_layer(torch, steps, warmup, batch=2, seq=4096):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    res = {}
-    for fp8 in (True, False):
-        lay = DecoderLayer(fp8=fp8, seed=5)
-        res[fp8] = t(lay)
-        if fp8:
-            spans = []
+    def linear_share(lay):
+        spans = []
 
-            def pre(mod, *a):
-                e = mk()
-                e.record()
-                spans.append([e, None])
+        def pre(mod, *a):
+            e = mk()
+            e.record()
+            spans.append([e, None])
 
-            def post(mod, *a):
-                e = mk()
-                e.record()
-                spans[-1][1] = e
-            hooks = []
-            for lin in lay.linears():
-                hooks += [lin.register_forward_pre_hook(pre), lin.register_forward_hook(post),
-                          lin.register_full_backward_pre_hook(pre), lin.register_full_backward_hook(post)]
-            run(lay, warmup)
-            torch.cuda.synchronize()
-            spans.clear()
-            e0, e1 = mk(), mk()
-            e0.record()
-            run(lay, steps)
-            e1.record()
-            torch.cuda.synchronize()
-            hooked_ms = e0.elapsed_time(e1) / steps
-            lin_ms = sum(a.elapsed_time(b) for a, b in spans) / steps
-            for h in hooks:
-                h.remove()
-        del lay
-        torch.cuda.empty_cache()
+        def post(mod, *a):
+            e = mk()
+            e.record()
+            spans[-1][1] = e
+        hooks = []
+        for lin in lay.linears():
+            hooks += [lin.register_forward_pre_hook(pre), lin.register_forward_hook(post),
+                      lin.register_full_backward_pre_hook(pre), lin.register_full_backward_hook(post)]
+        run(lay, warmup)
+        torch.cuda.synchronize()
+        spans.clear()
+        e0, e1 = mk(), mk()
+        e0.record()
+        run(lay, steps)
+        e1.record()
+        torch.cuda.synchronize()
+        total = e0.elapsed_time(e1) / steps
+        lin_ms = sum(a.elapsed_time(b) for a, b in spans) / steps
+        for h in hooks:
+            h.remove()
+        return lin_ms, lin_ms / total
+
     tokens = batch * seq
     lin_flops = 3 * 2 * tokens * (2048 * (4096 + 2048 + 12288) + 6144 * 2048)
     attn_flops = 3.5 * 4 * batch * seq * seq * 16 * 128 / 2
-    return {"tokens": tokens, "batch": batch, "seq": seq,
-            "fp8_layer_ms": round(res[True], 3), "bf16_layer_ms": round(res[False], 3),
-            "speedup_fp8_vs_bf16_layer": round(res[False] / res[True], 3),
-            "fp8_linears_ms": round(lin_ms, 3), "fp8_linears_share_of_layer_time": round(lin_ms / hooked_ms, 3),
-            "linears_share_of_layer_flops": round(lin_flops / (lin_flops + attn_flops), 3),
-            "note": "fwd+bwd; attention is PyTorch SDPA (causal, GQA) in BF16, norms/RoPE/SwiGLU PyTorch BF16; "
-                    "linears' time from events around each Fp8Linear forward and backward (hooked pass)"}
+    out = {"tokens": tokens, "batch": batch, "seq": seq}
+    for kind in ("fp8", "fp8_matrix_core", "bf16"):
+        lay = DecoderLayer(linears=kind, seed=5)
+        ms = t(lay)
+        lin_ms, share = linear_share(lay)
+        out[kind] = {"layer_ms": round(ms, 3), "linears_ms": round(lin_ms, 3),
+                     "linears_tflops": round(lin_flops / (lin_ms * 1e-3) / 1e12, 1),
+                     "linears_share_of_layer_time": round(share, 3)}
+        del lay
+        torch.cuda.empty_cache()
+    for kind in ("fp8", "fp8_matrix_core"):
+        out[kind]["layer_speedup_vs_bf16"] = round(out["bf16"]["layer_ms"] / out[kind]["layer_ms"], 3)
+        out[kind]["linears_speedup_vs_bf16"] = round(out["bf16"]["linears_ms"] / out[kind]["linears_ms"], 3)
+    out["linears_share_of_layer_flops"] = round(lin_flops / (lin_flops + attn_flops), 3)
+    out["note"] = ("fwd+bwd; attention is PyTorch SDPA (causal, GQA) in BF16, norms/RoPE/SwiGLU PyTorch BF16; "
+                   "linears' time from events around each linear's forward and backward (hooked pass); "
+                   "FP8 linears include their quantisers and FP32 main_grad accumulation")
+    return out
 
 
 def copy_probe(torch, dev, mib):

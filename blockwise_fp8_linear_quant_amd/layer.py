@@ -14,8 +14,9 @@ Layer (Qwen3 layout, 16 query heads and 8 key/value heads of 128):
     h2 = RMSNorm(x1)                   g, u = split(gate_up(h2))
     y  = x1 + down(silu(g) * u)
 
-The four linears are Fp8Linear (this library) or, for comparison, BF16
-nn.Linear.  Attention is PyTorch's scaled_dot_product_attention in BF16 (its
+The four linears are Fp8Linear (this library; exact block products, or the
+FP8 matrix instructions with linears="fp8_matrix_core") or, for comparison,
+BF16 nn.Linear (linears="bf16").  Attention is PyTorch's scaled_dot_product_attention in BF16 (its
 softmax accumulates in FP32); the other element-wise steps are PyTorch BF16
 operations.  Only the linears are the subject of this library.
 """
@@ -46,8 +47,11 @@ def apply_rope(t, cos, sin):
 
 
 class DecoderLayer(torch.nn.Module):
-    def __init__(self, fp8=True, device="cuda", seed=0):
+    def __init__(self, linears="fp8", device="cuda", seed=0):
         super().__init__()
+        if linears not in ("fp8", "fp8_matrix_core", "bf16"):
+            raise ValueError(f"linears must be 'fp8', 'fp8_matrix_core' or 'bf16', not {linears!r}")
+        fp8 = linears != "bf16"
         g = torch.Generator(device="cpu").manual_seed(seed)
 
         def weight(n, k):
@@ -56,7 +60,7 @@ class DecoderLayer(torch.nn.Module):
         def linear(k, n):
             w = weight(n, k)
             if fp8:
-                return Fp8Linear(k, n, weight=w)
+                return Fp8Linear(k, n, weight=w, fp8_matrix_core=(linears == "fp8_matrix_core"))
             lin = torch.nn.Linear(k, n, bias=False, device=device, dtype=torch.bfloat16)
             with torch.no_grad():
                 lin.weight.copy_(w)

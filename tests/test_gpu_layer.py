@@ -14,6 +14,8 @@ one-ulp difference upstream into a whole FP8 step downstream (on the CPU, one
 BF16 ulp added to 10% of the layer's input moves the reference output by 4%
 norm-wise), so the bound is 8%; wiring mistakes (a swapped split, a wrong
 key/value head, a missing mask) are off by order one.
+The same stage checks run with the FP8 matrix-instruction linears, whose
+GEMMs are held to the derived bound (2^-10 + 1e-5) * sum |a*b| instead.
 The backward pass is checked against the same layer with BF16 nn.Linear
 weights: finite gradients and cosine similarity above 0.99 for the input
 gradient and every weight gradient (the FP8 linears' main_grad).
@@ -55,22 +57,26 @@ def run():
     g = torch.Generator().manual_seed(11)
     x0 = (torch.randn((1, s, 2048), generator=g) * 0.5).to(torch.bfloat16).cuda()
     out = {}
-    for fp8 in (True, False):
-        lay = DecoderLayer(fp8=fp8, seed=3)
+    for kind in ("fp8", "fp8_matrix_core", "bf16"):
+        lay = DecoderLayer(linears=kind, seed=3)
         x = x0.clone().requires_grad_(True)
         tr = {}
-        say("decoder layer forward", "fp8" if fp8 else "bf16", s)
+        say("decoder layer forward", kind, s)
         y = lay(x, trace=tr)
-        say("decoder layer backward", "fp8" if fp8 else "bf16", s)
+        say("decoder layer backward", kind, s)
         y.float().pow(2).mean().backward()
         torch.cuda.synchronize()
-        grads = [l.weight.main_grad if fp8 else l.weight.grad for l in lay.linears()]
-        out[fp8] = dict(lay=lay, x=x, y=y.detach(), trace=tr, dx=x.grad, grads=grads)
+        grads = [l.weight.grad if kind == "bf16" else l.weight.main_grad for l in lay.linears()]
+        out[kind] = dict(lay=lay, x=x, y=y.detach(), trace=tr, dx=x.grad, grads=grads)
     return out
 
 
-def test_layer_stages(run):
-    r = run[True]
+FP8_PATH_RTOL = 2.0 ** -10 + 1e-5
+
+
+@pytest.mark.parametrize("kind,rtol", [("fp8", compare.FP32_RTOL), ("fp8_matrix_core", FP8_PATH_RTOL)])
+def test_layer_stages(run, kind, rtol):
+    r = run[kind]
     tr, lay = r["trace"], r["lay"]
     x = _vals(r["x"].detach()[0])
     w = [host(l.weight.detach()) for l in lay.linears()]
@@ -80,7 +86,7 @@ def test_layer_stages(run):
     _within(T["h"], ref.rms_norm(x), ulp(T["h"]), "rmsnorm 1")
     for name, inp, wi in (("qkv", "h", 0), ("o", "a", 1), ("gu", "h2", 2), ("down", "act", 3)):
         y, bnd = ref.fp8_linear(T[inp], w[wi], budget=True)
-        ok, rep = compare.check_bf16(host(tr[name][0].contiguous()), y, bnd)
+        ok, rep = compare.check_bf16(host(tr[name][0].contiguous()), y, bnd, rtol=rtol)
         assert ok, (name, rep)
 
     q, k, v = ref.split_heads(T["qkv"])
@@ -104,7 +110,7 @@ def test_layer_stages(run):
 
 
 def test_layer_chained_output(run):
-    r = run[True]
+    r = run["fp8"]
     x = host(r["x"].detach()[0])
     w = [host(l.weight.detach()) for l in r["lay"].linears()]
     want = ref.forward(x, *w)
@@ -113,9 +119,10 @@ def test_layer_chained_output(run):
     assert rel < 8e-2, rel
 
 
-def test_layer_backward_against_bf16_layer(run):
+@pytest.mark.parametrize("kind", ["fp8", "fp8_matrix_core"])
+def test_layer_backward_against_bf16_layer(run, kind):
     import torch
-    f, b = run[True], run[False]
+    f, b = run[kind], run["bf16"]
     assert torch.isfinite(f["dx"]).all()
     c = _cos(f["dx"], b["dx"])
     assert c > 0.99, ("dx", c)

@@ -3,8 +3,9 @@
 One linear of the M=4096 layer shape family at a smaller token count: the
 forward output, the data gradient and the FP32 weight gradient accumulated
 over two micro-batches are checked element by element against the float64
-oracle (same acceptance rule as the GEMM tests), and the FP8 weight cache is
-checked to rebuild exactly when the weight changes.
+oracle (same acceptance rule as the GEMM tests; with the FP8 matrix
+instructions, the derived bound (2^-10 + 1e-5) * sum |a*b|), and the FP8
+weight cache is checked to rebuild exactly when the weight changes.
 """
 
 import numpy as np
@@ -35,30 +36,31 @@ def _oracle_step(xb, wb, dyb):
     return (gemm.fwd(xq, sx, wq, sw), gemm.dgrad(dyq, sdy, wqT, swT), gemm.wgrad(dyqT, sdyT, xqT, sxT))
 
 
-def test_fp8_linear_forward_backward_two_microbatches(torch_mod):
+@pytest.mark.parametrize("mc,rtol", [(False, compare.FP32_RTOL), (True, 2.0 ** -10 + 1e-5)])
+def test_fp8_linear_forward_backward_two_microbatches(torch_mod, mc, rtol):
     torch = torch_mod
     from blockwise_fp8_linear_quant_amd.linear import Fp8Linear
     M, K, N = 300, 256, 384          # ragged token count, several tiles
     wb = W.normal_bf16((N, K), 0.02, W.seed_for(2, 1, "qkv", "w"))
-    lin = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous())
+    lin = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous(), fp8_matrix_core=mc)
     dw_sum = None
     bnd_sum = None
     for mb in range(2):
         xb = W.normal_bf16((M, K), 1.0, W.seed_for(2, 10 + mb, "qkv", "x"))
         dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(2, 10 + mb, "qkv", "dy"))
         x = dev_bf16(xb).contiguous().requires_grad_(True)
-        say("Fp8Linear micro-batch", mb, M, K, N)
+        say("Fp8Linear micro-batch", mb, M, K, N, "matrix core" if mc else "exact")
         y = lin(x)
         y.backward(dev_bf16(dyb).contiguous())
         torch.cuda.synchronize()
         (yy, yb), (dxx, dxb), (dww, dwb) = _oracle_step(xb, wb, dyb)
-        ok, rep = compare.check_bf16(host(y.detach()), yy, yb)
+        ok, rep = compare.check_bf16(host(y.detach()), yy, yb, rtol=rtol)
         assert ok, ("forward", mb, rep)
-        ok, rep = compare.check_bf16(host(x.grad), dxx, dxb)
+        ok, rep = compare.check_bf16(host(x.grad), dxx, dxb, rtol=rtol)
         assert ok, ("dgrad", mb, rep)
         dw_sum = dww if dw_sum is None else dw_sum + dww
         bnd_sum = dwb if bnd_sum is None else bnd_sum + dwb
-    ok, rep = compare.check_fp32(host(lin.weight.main_grad), dw_sum, bnd_sum)
+    ok, rep = compare.check_fp32(host(lin.weight.main_grad), dw_sum, bnd_sum, rtol=rtol)
     assert ok, ("wgrad accumulated", rep)
     assert lin.weight.grad is None
     assert lin.weight_quantisations == 1      # one FP8 weight for both micro-batches
