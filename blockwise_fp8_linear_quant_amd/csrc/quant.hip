@@ -48,6 +48,12 @@ __device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ row, int64_t
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Eight BF16 values at p (the caller guarantees they are all in bounds).
+__device__ __forceinline__ uint4 load8_full(const uint16_t* __restrict__ p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float elem(const uint4& v, int i) {
   const uint32_t w = (i >> 1) == 0 ? v.x : (i >> 1) == 1 ? v.y : (i >> 1) == 2 ? v.z : v.w;
   return (i & 1) ? bits_f32(w & 0xffff0000u) : bits_f32(w << 16);
@@ -302,6 +308,7 @@ struct SrcPlain {   // a BF16 tensor
   const uint16_t* x;
   int64_t ldx;
   __device__ __forceinline__ uint4 load(int64_t r, int64_t c0, int64_t C) const { return load8(x + r * ldx, c0, C); }
+  __device__ __forceinline__ uint4 load_full(int64_t r, int64_t c0) const { return load8_full(x + r * ldx + c0); }
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -317,7 +324,12 @@ struct SrcSwiGLU {
   const uint16_t* u;
   int64_t ldu;
   __device__ __forceinline__ uint4 load(int64_t r, int64_t c0, int64_t C) const {
-    const uint4 a = load8(g + r * ldg, c0, C), b = load8(u + r * ldu, c0, C);
+    return combine(load8(g + r * ldg, c0, C), load8(u + r * ldu, c0, C));
+  }
+  __device__ __forceinline__ uint4 load_full(int64_t r, int64_t c0) const {
+    return combine(load8_full(g + r * ldg + c0), load8_full(u + r * ldu + c0));
+  }
+  __device__ __forceinline__ uint4 combine(const uint4 a, const uint4 b) const {
     float h[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -336,8 +348,12 @@ struct SrcRMSNorm {
   const float* rstd;
   const uint16_t* gamma;
   __device__ __forceinline__ uint4 load(int64_t r, int64_t c0, int64_t C) const {
-    const uint4 a = load8(x + r * ldx, c0, C), w = load8(gamma, c0, C);
-    const float rs = rstd[r];
+    return combine(load8(x + r * ldx, c0, C), load8(gamma, c0, C), rstd[r]);
+  }
+  __device__ __forceinline__ uint4 load_full(int64_t r, int64_t c0) const {
+    return combine(load8_full(x + r * ldx + c0), load8_full(gamma + c0), rstd[r]);
+  }
+  __device__ __forceinline__ uint4 combine(const uint4 a, const uint4 w, const float rs) const {
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = (elem(a, j) * rs) * elem(w, j);
@@ -345,45 +361,18 @@ struct SrcRMSNorm {
   }
 };
 
-// The dual quantiser over any element source.  `hout` (optional, BF16
-// [R, ld_h]) receives the source values themselves -- for a fused producer,
-// the BF16 tensor it would otherwise have written.
-template <class Src>
-__global__ __launch_bounds__(256) void quant_dual_kernel(
-    Src src, int64_t R, int64_t C,
+// Maxima, codes and stores of one 128x128 tile whose values thread (rb, c)
+// holds in v[8] (rows 8rb..8rb+7, columns 8c..8c+7).  cred: this tile's
+// column-maximum exchange buffer.
+template <bool FULL>
+__device__ __forceinline__ void dual_encode(
+    const uint4 (&v)[8], int64_t br, int64_t bc, int64_t R, int64_t C,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
-    uint16_t* __restrict__ hout, int64_t ldh) {
-  __shared__ float cred[4][128];
-  __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
+    float (*cred)[128], const SetupEntry* stab) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  if (t < 128) stab[t] = setup_entry(t);
-  const int64_t br = blockIdx.y, bc = blockIdx.x;
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
-
-  uint4 v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t r = r0 + i;
-    v[i] = (r < R && c0 < C) ? src.load(r, c0, C) : make_uint4(0, 0, 0, 0);
-  }
-  if (hout != nullptr) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = r0 + i;
-      if (r < R && c0 < C) {
-        uint16_t* p = hout + r * ldh + c0;
-        if (c0 + 8 <= C) {
-          *reinterpret_cast<uint4*>(p) = v[i];
-        } else {
-          const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-          for (int j = 0; j < 8; ++j)
-            if (c0 + j < C) p[j] = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
-        }
-      }
-    }
-  }
   // Column maxima of this thread's 8 columns over its 8 rows, then over the
   // 4 row blocks of the wave (lanes 16 and 32 apart), then over the waves.
   float cm[8];
@@ -410,35 +399,44 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
     m = max8(m);
     rm[i] = dpp_fmax<kRor8>(m);
   }
-  __syncthreads();
+  // LDS-only barrier (lgkmcnt(0), then s_barrier): __syncthreads() would also
+  // make every wave wait for its outstanding global stores (the optional BF16
+  // output of a fused producer).
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x3 << 14));   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     cm[j] = fmaxf(fmaxf(cred[0][c * 8 + j], cred[1][c * 8 + j]), fmaxf(cred[2][c * 8 + j], cred[3][c * 8 + j]));
 
-  // Row-wise codes and scales.
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const GroupQ gq = group_setup_bf16(rm[i], stab);
-    const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
-    const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gq);
-    const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gq);
-    const int64_t r = r0 + i;
-    if (r < R && c0 < C) {
-      store8(q + r * ldq + c0, c0, C, lo, hi);
-      if (c == 0) s[bc * lds + r] = gq.s;
-    }
-  }
-  // Token-dimension codes: row-major words with per-column scales, then 4x4
-  // byte transposes into words of 4 tokens each.
+  // Column groups: scales out, constants kept; then each row is set up,
+  // encoded both ways and its row-wise codes stored.
   GroupQ gc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) gc[j] = group_setup_bf16(cm[j], stab);
-  uint32_t rw[8][2];
+  for (int j = 0; j < 8; ++j) {
+    gc[j] = group_setup_bf16(cm[j], stab);
+    if ((FULL || c0 + j < C) && rb == 0) sT[br * ldsT + c0 + j] = gc[j].s;
+  }
+  uint32_t rw[8][2];           // token-dimension codes, row-major (column scales)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    const GroupQ g = group_setup_bf16(rm[i], stab);
+    const uint32_t keep = (g.s == 0.0f) ? 0u : 0xffffffffu;
+    const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
+    const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
     rw[i][0] = code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
     rw[i][1] = code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
+    const int64_t r = r0 + i;
+    if (FULL) {
+      *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
+      if (c == 0) s[bc * lds + r] = g.s;
+    } else if (r < R && c0 < C) {
+      store8(q + r * ldq + c0, c0, C, lo, hi);
+      if (c == 0) s[bc * lds + r] = g.s;
+    }
   }
+  // Token-dimension codes: 4x4 byte transposes into words of 4 tokens each.
   uint32_t cw[8][2];
 #pragma unroll
   for (int rb2 = 0; rb2 < 2; ++rb2)
@@ -451,12 +449,57 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       for (int j = 0; j < 4; ++j) cw[4 * hh + j][rb2] = cc[j];
     }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (c0 + j < C) {
-      *reinterpret_cast<uint2*>(qT + (c0 + j) * ldqT + r0) = make_uint2(cw[j][0], cw[j][1]);
-      if (rb == 0) sT[br * ldsT + c0 + j] = gc[j].s;
+  for (int j = 0; j < 8; ++j)
+    if (FULL || c0 + j < C) *reinterpret_cast<uint2*>(qT + (c0 + j) * ldqT + r0) = make_uint2(cw[j][0], cw[j][1]);
+}
+
+// The dual quantiser over any element source, one 128x128 tile (blockIdx.y,
+// blockIdx.x) per workgroup; interior tiles take unguarded loads and stores.
+// `hout` (optional, BF16 [R, ld_h]) receives the source values themselves --
+// for a fused producer, the BF16 tensor it would otherwise have written.
+template <class Src>
+__global__ __launch_bounds__(256) void quant_dual_kernel(
+    Src src, int64_t R, int64_t C,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
+    uint16_t* __restrict__ hout, int64_t ldh) {
+  __shared__ float cred[4][128];
+  __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
+  const int t = threadIdx.x;
+  if (t < 128) stab[t] = setup_entry(t);
+  const int64_t br = blockIdx.y, bc = blockIdx.x;
+  const bool full = (br + 1) * 128 <= R && (bc + 1) * 128 <= C;
+  const int c = t & 15, rb = t >> 4;
+  const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
+  uint4 v[8];
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src.load_full(r0 + i, c0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + i;
+      v[i] = (r < R && c0 < C) ? src.load(r, c0, C) : make_uint4(0, 0, 0, 0);
     }
   }
+  if (hout != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + i;
+      if (r < R && c0 < C) {
+        uint16_t* p = hout + r * ldh + c0;
+        if (c0 + 8 <= C) {
+          *reinterpret_cast<uint4*>(p) = v[i];
+        } else {
+          const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          for (int j = 0; j < 8; ++j)
+            if (c0 + j < C) p[j] = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+        }
+      }
+    }
+  }
+  if (full) dual_encode<true>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab);
+  else dual_encode<false>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab);
 }
 
 // RMSNorm statistics: rstd[r] = 1 / sqrt(mean_c x[r, c]^2 + eps) in binary32,
