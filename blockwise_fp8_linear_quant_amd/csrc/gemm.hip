@@ -280,6 +280,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     for (int mt = 0; mt < MT; ++mt) qa[slot][mt] = lds16(buf, wm * WM + mt * 32 + rr, 4 * h + c);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) qb[slot][nt] = lds16(buf + BM * BK, wn * WN + nt * 32 + rr, 4 * h + c);
+    // Only VALU and SALU work may be scheduled across this point: the reads
+    // stay a slice ahead instead of sinking next to their first use.
+    __builtin_amdgcn_sched_barrier(0x0006);
   };
   auto convert = [&](int slot) {
 #pragma unroll
@@ -725,14 +728,17 @@ void launch_cfg(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
 }
 
 // Tile choice: 256 x 128 output tiles (8 waves of 64 x 64, triple-buffered
-// LDS, one workgroup per CU) when they still give every CU a tile; otherwise
-// 128 x 128 tiles (4 waves, double-buffered, two workgroups per CU).
+// LDS, one workgroup per CU) when they fill every CU for a whole number of
+// rounds; otherwise 128 x 128 tiles (4 waves, double-buffered, two
+// workgroups per CU), whose finer granularity keeps every CU busy in a
+// partial last round (e.g. 384 large tiles would leave half the CUs idle
+// for a third of the time).
 template <int SB_MODE, int OUT, int PREC>
 void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                  const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
                  int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
   const int64_t big_tiles = ((I + 255) / 256) * (J / 128);
-  if (big_tiles >= kCUs)
+  if (big_tiles >= kCUs && big_tiles % kCUs == 0)
     launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
   else
     launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC, 4, 2>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
