@@ -107,6 +107,42 @@ __device__ __forceinline__ void store8(uint8_t* __restrict__ p, int64_t col, int
     if (col + i < C) p[i] = (uint8_t)(((i < 4) ? lo : hi) >> ((i & 3) * 8));
 }
 
+// LDS-only workgroup barrier: lgkmcnt(0), then s_barrier.  __syncthreads()
+// would also make every wave wait for its outstanding global stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x3 << 14));   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Transposed codes of a 128x128 tile.  Thread (rb, c) = (t / 16, t % 16)
+// holds, in cw[j], the 8 codes of column 8c + j for tile rows 8rb .. 8rb + 7.
+// Written straight to global memory those are 8-byte pieces 32 bytes apart;
+// instead the tile goes through `stage` (16 KB of LDS) so that every column's
+// 128 bytes leave as 8 consecutive lanes x 16 bytes.  Row `col` of the stage
+// holds 16 slots of 8 bytes, slot s at s ^ 2((col / 8) % 8): 16-byte pairs stay
+// together and a wave's writes spread over the banks.  dst points at column 0,
+// row 0 of the tile (rows contiguous, ld bytes between columns); columns at or
+// beyond ncols are not written.  All 256 threads must call it.
+__device__ __forceinline__ void store_codes_transposed(const uint32_t (&cw)[8][2], uint4* stage, uint8_t* dst,
+                                                       int64_t ld, int64_t ncols) {
+  const int t = threadIdx.x, c = t & 15, rb = t >> 4;
+  uint8_t* st = reinterpret_cast<uint8_t*>(stage);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int col = 8 * c + j;
+    *reinterpret_cast<uint2*>(st + col * 128 + (rb ^ (2 * (c & 7))) * 8) = make_uint2(cw[j][0], cw[j][1]);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int id = t + 256 * u, col = id >> 3, k = id & 7;
+    const uint4 w = *reinterpret_cast<const uint4*>(st + col * 128 + ((2 * k) ^ (2 * ((col >> 3) & 7))) * 8);
+    if (col < ncols) *reinterpret_cast<uint4*>(dst + col * ld + 16 * k) = w;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row-wise 1x128: a wave quantises 8 rows x one 128-column group; lane (r, c)
 // with r = lane/8, c = lane%8 holds columns [8c, 8c+8) and [64+8c, 64+8c+8)
@@ -214,6 +250,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT) {
   __shared__ float red[4];
+  __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t br = blockIdx.y, bc = blockIdx.x;
   const int c = t & 15, rb = t >> 4;
@@ -264,9 +301,14 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) cw[4 * hh + j][rb2] = cc[j];
       }
+    if ((br + 1) * 128 <= R) {
+      // Whole 128-row block: every column's 128 codes are in range.
+      store_codes_transposed(cw, stage, qT + bc * 128 * ldqT + br * 128, ldqT, C - bc * 128);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < C && r0 < R) store8(qT + (c0 + j) * ldqT + r0, r0, R, cw[j][0], cw[j][1]);
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < C && r0 < R) store8(qT + (c0 + j) * ldqT + r0, r0, R, cw[j][0], cw[j][1]);
+    }
   }
   if (t == 0) {
     const int64_t nbr = (R + 127) / 128, nbc = (C + 127) / 128;
@@ -369,7 +411,7 @@ __device__ __forceinline__ void dual_encode(
     const uint4 (&v)[8], int64_t br, int64_t bc, int64_t R, int64_t C,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
-    float (*cred)[128], const SetupEntry* stab) {
+    float (*cred)[128], const SetupEntry* stab, uint4* stage) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
@@ -399,13 +441,8 @@ __device__ __forceinline__ void dual_encode(
     m = max8(m);
     rm[i] = dpp_fmax<kRor8>(m);
   }
-  // LDS-only barrier (lgkmcnt(0), then s_barrier): __syncthreads() would also
-  // make every wave wait for its outstanding global stores (the optional BF16
-  // output of a fused producer).
-  __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x3 << 14));   // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  // LDS-only barrier, so that a fused producer's BF16 stores stay in flight.
+  lds_barrier();
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     cm[j] = fmaxf(fmaxf(cred[0][c * 8 + j], cred[1][c * 8 + j]), fmaxf(cred[2][c * 8 + j], cred[3][c * 8 + j]));
@@ -448,9 +485,8 @@ __device__ __forceinline__ void dual_encode(
 #pragma unroll
       for (int j = 0; j < 4; ++j) cw[4 * hh + j][rb2] = cc[j];
     }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (FULL || c0 + j < C) *reinterpret_cast<uint2*>(qT + (c0 + j) * ldqT + r0) = make_uint2(cw[j][0], cw[j][1]);
+  // Token rows past R hold 0x00 codes: the padded layout stores them as pads.
+  store_codes_transposed(cw, stage, qT + bc * 128 * ldqT + br * 128, ldqT, FULL ? 128 : C - bc * 128);
 }
 
 // The dual quantiser over any element source, one 128x128 tile (blockIdx.y,
@@ -465,6 +501,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
     uint16_t* __restrict__ hout, int64_t ldh) {
   __shared__ float cred[4][128];
   __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
+  __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
   const int t = threadIdx.x;
   if (t < 128) stab[t] = setup_entry(t);
   const int64_t br = blockIdx.y, bc = blockIdx.x;
@@ -498,8 +535,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       }
     }
   }
-  if (full) dual_encode<true>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab);
-  else dual_encode<false>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab);
+  if (full) dual_encode<true>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage);
+  else dual_encode<false>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage);
 }
 
 // RMSNorm statistics: rstd[r] = 1 / sqrt(mean_c x[r, c]^2 + eps) in binary32,
