@@ -336,12 +336,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
 // come out as 0x00 pads in qT.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t code4_each(float a, float b, float c, float d, const GroupQ (&g)[8], int j0) {
-  // Four values of one row, columns j0..j0+3, each with its own column's scale.
-  const float q0 = g[j0 + 0].s == 0.0f ? 0.0f : group_quotient(a, g[j0 + 0]);
-  const float q1 = g[j0 + 1].s == 0.0f ? 0.0f : group_quotient(b, g[j0 + 1]);
-  const float q2 = g[j0 + 2].s == 0.0f ? 0.0f : group_quotient(c, g[j0 + 2]);
-  const float q3 = g[j0 + 3].s == 0.0f ? 0.0f : group_quotient(d, g[j0 + 3]);
-  return enc4(q0, q1, q2, q3);
+  // Four values of one row, columns j0..j0+3, each with its own column's
+  // scale.  A zero column group has s_n = r_n = 1, k = 0 and only +-0
+  // elements, so its quotients are +-0; the caller masks those bytes to 0x00.
+  return enc4(group_quotient(a, g[j0 + 0]), group_quotient(b, g[j0 + 1]), group_quotient(c, g[j0 + 2]),
+              group_quotient(d, g[j0 + 3]));
 }
 
 // Element sources of the dual quantiser: eight BF16 values (bit patterns) of
@@ -450,9 +449,11 @@ __device__ __forceinline__ void dual_encode(
   // Column groups: scales out, constants kept; then each row is set up,
   // encoded both ways and its row-wise codes stored.
   GroupQ gc[8];
+  uint32_t cmask[2] = {0u, 0u};   // 0xFF for the bytes of non-zero column groups
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     gc[j] = group_setup_bf16(cm[j], stab);
+    if (gc[j].s != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
     if ((FULL || c0 + j < C) && rb == 0) sT[br * ldsT + c0 + j] = gc[j].s;
   }
   uint32_t rw[8][2];           // token-dimension codes, row-major (column scales)
@@ -462,8 +463,8 @@ __device__ __forceinline__ void dual_encode(
     const uint32_t keep = (g.s == 0.0f) ? 0u : 0xffffffffu;
     const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
     const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
-    rw[i][0] = code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
-    rw[i][1] = code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
+    rw[i][0] = cmask[0] & code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
+    rw[i][1] = cmask[1] & code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
     const int64_t r = r0 + i;
     if (FULL) {
       *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
