@@ -96,6 +96,18 @@ def test_small_and_ragged_shapes(B, shape):
     check_blocks(B, bits, "small")
 
 
+@pytest.mark.parametrize("shape", [(256, 136), (384, 1000), (128, 8), (200, 264)])
+def test_ragged_columns_dual_and_blocks(B, shape):
+    """Column counts that are not multiples of 128, with whole and partial
+    128-row tiles: the transposed outputs of the dual and 128x128 quantisers
+    leave through a staged tile that must skip the missing columns."""
+    bits = W.normal_bf16(shape, 1.0, W.seed_for(91, shape[0], shape[1], "x"))
+    check_dual(B, bits, "ragged columns")
+    check_blocks(B, bits, "ragged columns")
+    check_dual(B, bits, "small")
+    check_blocks(B, bits, "small")
+
+
 def test_pow2_tie_case(B):
     g = {}
     for line in open(os.path.join(GOLDEN, "quant_pow2_tie.txt")):
