@@ -14,10 +14,16 @@ The traffic summary records a digest of the GEMM kernel's source and build
 flags; ``bench.py`` reports the figure only while that digest still matches,
 so a changed kernel never carries counters taken from an older one.
 
+* ``counters``: per-kernel shader counters (matrix-unit and VALU activity,
+  wave wait states) from one or more ``rocprofv3 --pmc`` passes of the same
+  command, normalised by the cycles ``GRBM_GUI_ACTIVE`` counts in each pass.
+
 Usage (on the CPU, after the profiler runs):
   python -m blockwise_fp8_linear_quant_amd.profiling stats KERNEL_STATS.csv OUT.txt --command "..."
   python -m blockwise_fp8_linear_quant_amd.profiling traffic FETCH.csv WRITE.csv OUT.txt \
       --copy-bytes N --command "..."
+  python -m blockwise_fp8_linear_quant_amd.profiling counters PASS1.csv [PASS2.csv ...] OUT.txt \
+      --kernels block_gemm_f16_kernel quant_dual_kernel --command "..."
 """
 
 import argparse
@@ -130,6 +136,86 @@ def traffic_summary(fetch_csv, write_csv, copy_bytes, command, algorithmic_bytes
     return "\n".join(lines) + "\n"
 
 
+# MI355X: 8 XCDs x 32 CUs x 4 SIMDs; a wave64 VALU instruction occupies its
+# SIMD for 4 cycles; F16/BF16 dense matrix peak 2.5 PFLOP/s at 2.4 GHz.
+N_XCD, N_SIMD, VALU_CYCLES, F16_PEAK_FLOP_PER_CYCLE = 8, 1024, 4, 2.5e15 / 2.4e9
+
+
+def counters_summary(csvs, kernels, command):
+    """Shader-counter ratios per kernel instantiation, averaged over its dispatches.
+
+    Each pass is a separate run of the same command, so dispatches are matched
+    by their id.  Cycles per dispatch come from GRBM_GUI_ACTIVE of the same
+    pass (it counts on every XCD: divided by 8), and SIMD-cycles are that times
+    the 1024 SIMDs.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD-cycles (it
+    counts 32 cycles per 32x32x16 F16 MFMA); VALU busy = non-MFMA VALU
+    instructions x 4 cycles / SIMD-cycles; wait fractions are per wave-cycle.
+    """
+    per = {}   # (dispatch, name) -> {counter: value, "_cyc_<pass>": cycles, "_dur": ns}
+    for ip, path in enumerate(csvs):
+        for r in csv.DictReader(open(path)):
+            name = short_name(r["Kernel_Name"])
+            if not any(k in name for k in kernels):
+                continue
+            key = (int(r["Dispatch_Id"]), name)
+            d = per.setdefault(key, {})
+            c, v = r["Counter_Name"], float(r["Counter_Value"])
+            if c == "GRBM_GUI_ACTIVE":
+                d[f"_cyc{ip}"] = d.get(f"_cyc{ip}", 0.0) + v / N_XCD
+                d[f"_dur{ip}"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            else:
+                d[c] = d.get(c, 0.0) + v
+                d[f"_pass_{c}"] = ip
+    groups = {}
+    for (_, name), d in per.items():
+        groups.setdefault(name, []).append(d)
+    lines = [f"command: {command}", ""]
+    for name, ds in sorted(groups.items()):
+        def ratio(num, den_fn):
+            vals = [d[num] / den_fn(d) for d in ds if num in d and den_fn(d)]
+            return sum(vals) / len(vals) if vals else None
+
+        def simd_cycles(c):
+            def f(d):
+                ip = d.get(f"_pass_{c}")
+                return d.get(f"_cyc{ip}", 0.0) * N_SIMD if ip is not None else 0.0
+            return f
+        clk = [d[f"_cyc{i}"] / d[f"_dur{i}"] for d in ds for i in range(len(csvs)) if f"_dur{i}" in d]
+        dur = [d[f"_dur{i}"] for d in ds for i in range(len(csvs)) if f"_dur{i}" in d]
+        lines.append(f"kernel: {name}")
+        lines.append(f"  dispatches: {len(ds)}")
+        if dur:
+            lines.append(f"  mean_duration_us (under the profiler): {sum(dur) / len(dur) / 1e3:.2f}")
+        if clk:
+            lines.append(f"  clock_ghz (GRBM_GUI_ACTIVE / 8 / duration): {sum(clk) / len(clk):.2f}")
+        vals = {
+            "mfma_busy": ratio("SQ_VALU_MFMA_BUSY_CYCLES", simd_cycles("SQ_VALU_MFMA_BUSY_CYCLES")),
+            "valu_mfma_coexec": ratio("SQ_VALU_MFMA_COEXEC_CYCLES", simd_cycles("SQ_VALU_MFMA_COEXEC_CYCLES")),
+        }
+        valu = [((d["SQ_INSTS_VALU"] - d.get("SQ_INSTS_MFMA", 0.0)) * VALU_CYCLES) / simd_cycles("SQ_INSTS_VALU")(d)
+                for d in ds if "SQ_INSTS_VALU" in d and simd_cycles("SQ_INSTS_VALU")(d)]
+        if valu:
+            vals["valu_busy (non-MFMA, 4 cycles per instruction)"] = sum(valu) / len(valu)
+        for k, v in vals.items():
+            if v is not None:
+                lines.append(f"  {k}: {v:.3f}")
+        for num, den, label in (("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "valu_instructions_per_mfma (incl. MFMA)"),
+                                ("SQ_INSTS_LDS", "SQ_INSTS_MFMA", "lds_instructions_per_mfma"),
+                                ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "wave_fraction_waiting_on_waitcnt_or_barrier"),
+                                ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "wave_fraction_ready_but_not_issued"),
+                                ("SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES", "wave_fraction_issuing"),
+                                ("SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "lds_bank_conflict_cycles_per_lds_instruction")):
+            v = ratio(num, lambda d, den=den: d.get(den, 0.0))
+            if v is not None:
+                lines.append(f"  {label}: {v:.3f}")
+        mf = [d["SQ_INSTS_MFMA"] for d in ds if "SQ_INSTS_MFMA" in d]
+        if mf and clk and "f16" in name:
+            flops = [d["SQ_INSTS_MFMA"] * 32768 for d in ds if "SQ_INSTS_MFMA" in d]
+            lines.append(f"  mfma_flop_per_dispatch (32x32x16 F16): {sum(flops) / len(flops):.4g}")
+        lines.append("")
+    return "\n".join(lines)
+
+
 def read_traffic(path):
     """The traffic summary as a dict, or None if missing or taken from another kernel source."""
     if not os.path.exists(path):
@@ -159,11 +245,19 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--algorithmic-bytes", type=float)
+    c = sub.add_parser("counters")
+    c.add_argument("csvs", nargs="+")
+    c.add_argument("--kernels", nargs="+", required=True)
+    c.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "stats":
         text = stats_summary(a.stats_csv, a.command, a.steps)
-    else:
+    elif a.cmd == "traffic":
         text = traffic_summary(a.fetch_csv, a.write_csv, a.copy_bytes, a.command, a.algorithmic_bytes)
+    else:
+        *inputs, out = a.csvs
+        a.out = out
+        text = counters_summary(inputs, a.kernels, a.command)
     with open(a.out, "w") as f:
         f.write(text)
     print(text, end="")
