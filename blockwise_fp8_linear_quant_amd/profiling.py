@@ -187,7 +187,8 @@ def counters_summary(csvs, kernels, command):
         if dur:
             lines.append(f"  mean_duration_us (under the profiler): {sum(dur) / len(dur) / 1e3:.2f}")
         if clk:
-            lines.append(f"  clock_ghz (GRBM_GUI_ACTIVE / 8 / duration): {sum(clk) / len(clk):.2f}")
+            lines.append(f"  clock_ghz (GRBM_GUI_ACTIVE / 8 / duration; overstated for dispatches of a few us): "
+                         f"{sum(clk) / len(clk):.2f}")
         vals = {
             "mfma_busy": ratio("SQ_VALU_MFMA_BUSY_CYCLES", simd_cycles("SQ_VALU_MFMA_BUSY_CYCLES")),
             "valu_mfma_coexec": ratio("SQ_VALU_MFMA_COEXEC_CYCLES", simd_cycles("SQ_VALU_MFMA_COEXEC_CYCLES")),
