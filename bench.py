@@ -416,7 +416,8 @@ def main():
             L.gemms(B, fp8_mc, evs[i][1:] if evs is not None else None)
 
     def timed(fp8_mc):
-        """K timed steps -> (ms/step, per-GEMM ms [linear][op], quantiser ms/step, wall s)."""
+        """K timed steps -> (ms/step, per-GEMM ms [linear][op], quantiser ms/step, wall s,
+        p10/p50/p90 over the steps of the 12 GEMM launches' summed time)."""
         for _ in range(args.warmup):
             step(fp8_mc=fp8_mc)
         torch.cuda.synchronize()
@@ -436,10 +437,14 @@ def main():
                      for o in range(3)] for i in range(len(layers))]
         quant_ms = sum(evs[s][i][0].elapsed_time(evs[s][i][1])
                        for s in range(args.steps) for i in range(len(layers))) / args.steps
-        return ms_step, per_gemm, quant_ms, t_wall
+        # Per-step sum of the 12 GEMM launches, for the spread across steps.
+        gemm_steps = sorted(sum(evs[s][i][o + 1].elapsed_time(evs[s][i][o + 2])
+                                for i in range(len(layers)) for o in range(3)) for s in range(args.steps))
+        pct = lambda q: gemm_steps[min(len(gemm_steps) - 1, int(q * (len(gemm_steps) - 1) + 0.5))]
+        return ms_step, per_gemm, quant_ms, t_wall, [pct(0.1), pct(0.5), pct(0.9)]
 
     # Timed region (default path: exact block products on the F16 matrix path).
-    ms_step, per_gemm, quant_ms, t_wall = timed(False)
+    ms_step, per_gemm, quant_ms, t_wall, gemm_spread = timed(False)
     flops = sum(L.flops() for L in layers)
     gemm_ms = sum(sum(r) for r in per_gemm)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -479,7 +484,7 @@ def main():
     fast = None
     f_gemm_ms = None
     if not args.no_fp8_path:
-        f_ms, f_gemm, f_q, _ = timed(True)
+        f_ms, f_gemm, f_q, _, _ = timed(True)
         f_gemm_ms = sum(sum(r) for r in f_gemm)
         fast = {"ms_per_step": round(f_ms, 4), "value": round(flops / (f_ms * 1e-3) / 1e12, 3),
                 "gemm_tflops": round(flops / (f_gemm_ms * 1e-3) / 1e12, 3),
@@ -511,6 +516,7 @@ def main():
                      "launches_per_step": n_launch,
                      "avg_launch_us": round(gemm_ms / n_launch * 1e3, 2),
                      "gemm_ms_per_step": round(gemm_ms, 4),
+                     "gemm_ms_per_step_p10_p50_p90": [round(v, 4) for v in gemm_spread],
                      "frac_of_fp8_peak": round(gemm_tflops / PEAK_TFLOPS["fp8"], 4)},
         "gemms": gemms,
         "quantisers": {"ms_per_step": round(quant_ms, 4), "algorithmic_gb": round(qbytes / 1e9, 4),
