@@ -358,8 +358,11 @@ def decoder_layer(torch, steps, warmup, batch=2, seq=4096):
     lin_flops = 3 * 2 * tokens * (2048 * (4096 + 2048 + 12288) + 6144 * 2048)
     attn_flops = 3.5 * 4 * batch * seq * seq * 16 * 128 / 2
     out = {"tokens": tokens, "batch": batch, "seq": seq}
-    for kind in ("fp8", "fp8_matrix_core", "bf16"):
-        lay = DecoderLayer(linears=kind, seed=5)
+    for kind in ("fp8", "fp8_unfused", "fp8_matrix_core", "bf16"):
+        if kind == "fp8_unfused":
+            lay = DecoderLayer(linears="fp8", seed=5, fused=False)
+        else:
+            lay = DecoderLayer(linears=kind, seed=5)
         ms = t(lay)
         lin_ms, share = linear_share(lay)
         out[kind] = {"layer_ms": round(ms, 3), "linears_ms": round(lin_ms, 3),
@@ -367,13 +370,17 @@ def decoder_layer(torch, steps, warmup, batch=2, seq=4096):
                      "linears_share_of_layer_time": round(share, 3)}
         del lay
         torch.cuda.empty_cache()
-    for kind in ("fp8", "fp8_matrix_core"):
+    for kind in ("fp8", "fp8_unfused", "fp8_matrix_core"):
         out[kind]["layer_speedup_vs_bf16"] = round(out["bf16"]["layer_ms"] / out[kind]["layer_ms"], 3)
         out[kind]["linears_speedup_vs_bf16"] = round(out["bf16"]["linears_ms"] / out[kind]["linears_ms"], 3)
     out["linears_share_of_layer_flops"] = round(lin_flops / (lin_flops + attn_flops), 3)
-    out["note"] = ("fwd+bwd; attention is PyTorch SDPA (causal, GQA) in BF16, norms/RoPE/SwiGLU PyTorch BF16; "
-                   "linears' time from events around each linear's forward and backward (hooked pass); "
-                   "FP8 linears include their quantisers and FP32 main_grad accumulation")
+    out["note"] = ("fwd+bwd; attention is PyTorch SDPA (causal, GQA) in BF16, RoPE and head norms PyTorch BF16; "
+                   "fp8 and fp8_matrix_core fuse the two RMSNorms and the SwiGLU into the next linear's quantiser "
+                   "(their backward by PyTorch kernels on a recomputed forward), fp8_unfused and bf16 run them as PyTorch "
+                   "BF16 ops; "
+                   "linears' time from events around each linear's forward and backward (hooked pass; for the "
+                   "fused kinds it includes the fused producers); FP8 linears include their quantisers and FP32 "
+                   "main_grad accumulation")
     return out
 
 

@@ -16,7 +16,9 @@ Layer (Qwen3 layout, 16 query heads and 8 key/value heads of 128):
 
 The four linears are Fp8Linear (this library; exact block products, or the
 FP8 matrix instructions with linears="fp8_matrix_core") or, for comparison,
-BF16 nn.Linear (linears="bf16").  Attention is PyTorch's scaled_dot_product_attention in BF16 (its
+BF16 nn.Linear (linears="bf16").  With FP8 linears the two RMSNorms and the
+SwiGLU are by default fused into the quantiser of the linear they feed
+(fused=False keeps them as separate PyTorch operations).  Attention is PyTorch's scaled_dot_product_attention in BF16 (its
 softmax accumulates in FP32); the other element-wise steps are PyTorch BF16
 operations.  Only the linears are the subject of this library.
 """
@@ -47,7 +49,7 @@ def apply_rope(t, cos, sin):
 
 
 class DecoderLayer(torch.nn.Module):
-    def __init__(self, linears="fp8", device="cuda", seed=0):
+    def __init__(self, linears="fp8", device="cuda", seed=0, fused=True):
         super().__init__()
         if linears not in ("fp8", "fp8_matrix_core", "bf16"):
             raise ValueError(f"linears must be 'fp8', 'fp8_matrix_core' or 'bf16', not {linears!r}")
@@ -67,6 +69,7 @@ class DecoderLayer(torch.nn.Module):
             return lin
 
         self.fp8 = fp8
+        self.fused = fused
         self.qkv = linear(HIDDEN, (HEADS + 2 * KV_HEADS) * HEAD_DIM)
         self.o = linear(HEADS * HEAD_DIM, HIDDEN)
         self.gate_up = linear(HIDDEN, 2 * INTER)
@@ -81,18 +84,32 @@ class DecoderLayer(torch.nn.Module):
 
     def forward(self, x, trace=None):
         """x [b, s, 2048] BF16 -> [b, s, 2048] BF16.  trace: optional dict that
-        receives the intermediate tensors (detached) under the names used above."""
+        receives the intermediate tensors (detached) under the names used above.
+
+        With FP8 linears and fused=True the two RMSNorms and the SwiGLU are
+        formed inside the following linear's quantiser (their BF16 values are
+        written out only when a trace is asked for)."""
         def keep(name, t):
             if trace is not None:
                 trace[name] = t.detach()
             return t
 
+        def bf16_out(cols):
+            return None if trace is None else torch.empty((b * s, cols), dtype=torch.bfloat16, device=x.device)
+
         b, s, _ = x.shape
         if s not in self._rope:
             self._rope[s] = rope_tables(s, x.device)
         cos, sin = self._rope[s]
-        h = keep("h", F.rms_norm(x, (HIDDEN,), self.norm1, EPS))
-        qkv = keep("qkv", self.qkv(h))
+        fused = self.fp8 and self.fused
+        if fused:
+            h = bf16_out(HIDDEN)
+            qkv = self.qkv.forward_rmsnorm(x, self.norm1, EPS, h_out=h)
+            if trace is not None:
+                keep("h", h.view(b, s, HIDDEN))
+        else:
+            qkv = self.qkv(keep("h", F.rms_norm(x, (HIDDEN,), self.norm1, EPS)))
+        keep("qkv", qkv)
         q, k, v = qkv.split([HEADS * HEAD_DIM, KV_HEADS * HEAD_DIM, KV_HEADS * HEAD_DIM], dim=-1)
         q = F.rms_norm(q.reshape(b, s, HEADS, HEAD_DIM), (HEAD_DIM,), self.q_norm, EPS).transpose(1, 2)
         k = F.rms_norm(k.reshape(b, s, KV_HEADS, HEAD_DIM), (HEAD_DIM,), self.k_norm, EPS).transpose(1, 2)
@@ -101,8 +118,17 @@ class DecoderLayer(torch.nn.Module):
         a = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
         a = keep("a", a.transpose(1, 2).reshape(b, s, HEADS * HEAD_DIM))
         x1 = keep("x1", x + keep("o", self.o(a)))
-        h2 = keep("h2", F.rms_norm(x1, (HIDDEN,), self.norm2, EPS))
-        gu = keep("gu", self.gate_up(h2))
-        gate, up = gu.split([INTER, INTER], dim=-1)
-        act = keep("act", F.silu(gate) * up)
-        return x1 + keep("down", self.down(act))
+        if fused:
+            h2 = bf16_out(HIDDEN)
+            gu = keep("gu", self.gate_up.forward_rmsnorm(x1, self.norm2, EPS, h_out=h2))
+            act = bf16_out(INTER)
+            down = self.down.forward_swiglu(gu, h_out=act)
+            if trace is not None:
+                keep("h2", h2.view(b, s, HIDDEN))
+                keep("act", act.view(b, s, INTER))
+        else:
+            h2 = keep("h2", F.rms_norm(x1, (HIDDEN,), self.norm2, EPS))
+            gu = keep("gu", self.gate_up(h2))
+            gate, up = gu.split([INTER, INTER], dim=-1)
+            down = self.down(keep("act", F.silu(gate) * up))
+        return x1 + keep("down", down)

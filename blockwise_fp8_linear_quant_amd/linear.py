@@ -21,6 +21,11 @@ library's kernels):
   weight value and reused by every micro-batch until the weight changes (the
   cache is keyed on the parameter's in-place version counter).
 
+Two fused entry points put the producer of the linear's input into its
+quantiser: ``forward_rmsnorm`` (RMSNorm, for the qkv and gate_up projections)
+and ``forward_swiglu`` (SwiGLU, for the down projection).  Their backward
+passes run the producer's backward with PyTorch's kernels from the saved inputs.
+
 The three GEMMs form each 128-wide block product exactly by default; with
 ``fp8_matrix_core=True`` they use the FP8 matrix instructions instead (about
 1.5 times the GEMM rate; the hardware truncates small products inside groups
@@ -28,6 +33,7 @@ of 8 positions, an error up to about 2^-10 of the block's sum of |a*b|).
 """
 
 import torch
+import torch.nn.functional as F
 
 from . import binding as B
 
@@ -70,16 +76,75 @@ class _Fp8LinearFn(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy):
         xqT, sxT = ctx.saved_tensors
-        weight = ctx.weight
-        _, _, wqT, swT = ctx.cache.get(weight)
-        dy = dy.contiguous()
-        dyq, sdy, dyqT, sdyT = B.fp8_quant_1x128_dual(dy)
-        dx = B.fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, fp8_matrix_core=ctx.mc)
-        if getattr(weight, "main_grad", None) is None:
-            weight.main_grad = torch.zeros(weight.shape, dtype=torch.float32, device=weight.device)
-        B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=ctx.M, dw=weight.main_grad, accumulate=True,
-                               fp8_matrix_core=ctx.mc)
-        return dx, None, None, None
+        return _linear_backward(ctx.cache, ctx.weight, xqT, sxT, ctx.M, ctx.mc, dy), None, None, None
+
+
+def _linear_backward(cache, weight, xqT, sxT, M, mc, dy):
+    """dY -> dX (BF16), accumulating dW into weight.main_grad (FP32)."""
+    _, _, wqT, swT = cache.get(weight)
+    dy = dy.contiguous()
+    dyq, sdy, dyqT, sdyT = B.fp8_quant_1x128_dual(dy)
+    dx = B.fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, fp8_matrix_core=mc)
+    if getattr(weight, "main_grad", None) is None:
+        weight.main_grad = torch.zeros(weight.shape, dtype=torch.float32, device=weight.device)
+    B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, dw=weight.main_grad, accumulate=True, fp8_matrix_core=mc)
+    return dx
+
+
+class _Fp8RMSNormLinearFn(torch.autograd.Function):
+    """y = RMSNorm(x; gamma, eps) . W^T with the normalisation fused into the
+    quantiser: the BF16 normalised value exists only in registers (or in the
+    optional h_out).  Backward: the linear's dgrad gives dL/dh, then PyTorch's
+    fused RMSNorm backward from x, gamma and the saved 1/rms."""
+
+    @staticmethod
+    def forward(ctx, x, gamma, weight, cache, mc, eps, h_out):
+        wq, sw, _, _ = cache.get(weight)
+        xq, sx, xqT, sxT, rstd = B.fp8_rmsnorm_quant_1x128_dual(x, gamma, eps, y_out=h_out)
+        y = B.fp8_block_gemm_fwd(xq, sx, wq, sw, fp8_matrix_core=mc)
+        ctx.save_for_backward(x, gamma, rstd, xqT, sxT)
+        ctx.cache, ctx.weight, ctx.M, ctx.mc = cache, weight, x.shape[0], mc
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, gamma, rstd, xqT, sxT = ctx.saved_tensors
+        dh = _linear_backward(ctx.cache, ctx.weight, xqT, sxT, ctx.M, ctx.mc, dy)
+        # The producer's backward: PyTorch's fused RMSNorm backward with the
+        # 1/rms the forward kernel wrote ([rows, 1] FP32, as PyTorch keeps it).
+        dx, dgamma = torch.ops.aten._fused_rms_norm_backward(dh, x, [x.shape[1]], rstd.view(-1, 1), gamma,
+                                                             [True, True])
+        return dx, dgamma, None, None, None, None, None
+
+
+class _Fp8SwiGLULinearFn(torch.autograd.Function):
+    """y = (silu(gate) * up) . W^T for gu = [gate | up] with the activation
+    fused into the quantiser.  Backward: the linear's dgrad gives dL/d(act),
+    then PyTorch's SwiGLU backward from the saved gate and up."""
+
+    @staticmethod
+    def forward(ctx, gu, weight, cache, mc, h_out):
+        wq, sw, _, _ = cache.get(weight)
+        half = gu.shape[1] // 2
+        gate, up = gu[:, :half], gu[:, half:]
+        aq, sa, aqT, saT = B.fp8_swiglu_quant_1x128_dual(gate, up, h_out=h_out)
+        y = B.fp8_block_gemm_fwd(aq, sa, wq, sw, fp8_matrix_core=mc)
+        ctx.save_for_backward(gu, aqT, saT)
+        ctx.cache, ctx.weight, ctx.M, ctx.mc = cache, weight, gu.shape[0], mc
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        gu, aqT, saT = ctx.saved_tensors
+        da = _linear_backward(ctx.cache, ctx.weight, aqT, saT, ctx.M, ctx.mc, dy)
+        # The producer's backward with PyTorch's SiLU kernels, written straight
+        # into the two halves of d[gate | up].
+        half = gu.shape[1] // 2
+        gate, up = gu[:, :half], gu[:, half:]
+        dgu = torch.empty_like(gu)
+        torch.ops.aten.silu_backward.grad_input(da * up, gate, grad_input=dgu[:, :half])
+        torch.mul(da, F.silu(gate), out=dgu[:, half:])
+        return dgu, None, None, None, None
 
 
 class Fp8Linear(torch.nn.Module):
@@ -109,10 +174,39 @@ class Fp8Linear(torch.nn.Module):
         """How many times the FP8 weight has been (re)built."""
         return self._cache.builds
 
-    def forward(self, x):
+    def forward(self, x, rmsnorm=None, swiglu=False, h_out=None):
+        """y = x . W^T for x [..., in_features] BF16.
+
+        rmsnorm=(gamma, eps): y = (RMSNorm(x) * gamma) . W^T with the
+        normalisation fused into the quantiser (gamma BF16 [in_features]).
+        swiglu=True: x = [gate | up] (2 * in_features wide) and
+        y = (silu(gate) * up) . W^T with the activation fused likewise.
+        h_out: optional BF16 [rows, in_features] receiving the fused producer's value.
+        """
         shape = x.shape
-        x2 = x.reshape(-1, self.in_features)
-        if x2.stride(1) != 1 or x2.stride(0) % 8 != 0 or x2.data_ptr() % 16 != 0:
-            x2 = x2.contiguous()
-        y = _Fp8LinearFn.apply(x2, self.weight, self._cache, self.fp8_matrix_core)
+        if rmsnorm is not None:
+            gamma, eps = rmsnorm
+            y = _Fp8RMSNormLinearFn.apply(_rows(x, self.in_features), gamma, self.weight, self._cache,
+                                          self.fp8_matrix_core, float(eps), h_out)
+        elif swiglu:
+            y = _Fp8SwiGLULinearFn.apply(_rows(x, 2 * self.in_features), self.weight, self._cache,
+                                         self.fp8_matrix_core, h_out)
+        else:
+            y = _Fp8LinearFn.apply(_rows(x, self.in_features), self.weight, self._cache, self.fp8_matrix_core)
         return y.reshape(*shape[:-1], self.out_features)
+
+    def forward_rmsnorm(self, x, gamma, eps, h_out=None):
+        """self(RMSNorm(x) * gamma), the normalisation fused into the quantiser."""
+        return self(x, rmsnorm=(gamma, eps), h_out=h_out)
+
+    def forward_swiglu(self, gu, h_out=None):
+        """self(silu(gate) * up) for gu = [gate | up], the activation fused into the quantiser."""
+        return self(gu, swiglu=True, h_out=h_out)
+
+
+def _rows(x, cols):
+    """x as a 2-D [rows, cols] BF16 view with unit column stride and 16-byte aligned rows."""
+    x2 = x.reshape(-1, cols)
+    if x2.stride(1) != 1 or x2.stride(0) % 8 != 0 or x2.data_ptr() % 16 != 0:
+        x2 = x2.contiguous()
+    return x2

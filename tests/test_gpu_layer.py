@@ -14,11 +14,14 @@ one-ulp difference upstream into a whole FP8 step downstream (on the CPU, one
 BF16 ulp added to 10% of the layer's input moves the reference output by 4%
 norm-wise), so the bound is 8%; wiring mistakes (a swapped split, a wrong
 key/value head, a missing mask) are off by order one.
-The same stage checks run with the FP8 matrix-instruction linears, whose
-GEMMs are held to the derived bound (2^-10 + 1e-5) * sum |a*b| instead.
+The same stage checks run with the producers (RMSNorm, SwiGLU) as separate
+PyTorch operations and fused into the linears' quantisers (the default), and
+with the FP8 matrix-instruction linears, whose GEMMs are held to the derived
+bound (2^-10 + 1e-5) * sum |a*b| instead.
 The backward pass is checked against the same layer with BF16 nn.Linear
 weights: finite gradients and cosine similarity above 0.99 for the input
-gradient and every weight gradient (the FP8 linears' main_grad).
+gradient, every weight gradient (the FP8 linears' main_grad) and the two
+RMSNorm gains.
 """
 
 import numpy as np
@@ -57,8 +60,11 @@ def run():
     g = torch.Generator().manual_seed(11)
     x0 = (torch.randn((1, s, 2048), generator=g) * 0.5).to(torch.bfloat16).cuda()
     out = {}
-    for kind in ("fp8", "fp8_matrix_core", "bf16"):
-        lay = DecoderLayer(linears=kind, seed=3)
+    for kind in ("fp8", "fp8_unfused", "fp8_matrix_core", "bf16"):
+        if kind == "fp8_unfused":
+            lay = DecoderLayer(linears="fp8", seed=3, fused=False)
+        else:
+            lay = DecoderLayer(linears=kind, seed=3)
         x = x0.clone().requires_grad_(True)
         tr = {}
         say("decoder layer forward", kind, s)
@@ -67,14 +73,16 @@ def run():
         y.float().pow(2).mean().backward()
         torch.cuda.synchronize()
         grads = [l.weight.grad if kind == "bf16" else l.weight.main_grad for l in lay.linears()]
-        out[kind] = dict(lay=lay, x=x, y=y.detach(), trace=tr, dx=x.grad, grads=grads)
+        norms = [lay.norm1.grad, lay.norm2.grad]
+        out[kind] = dict(lay=lay, x=x, y=y.detach(), trace=tr, dx=x.grad, grads=grads, norms=norms)
     return out
 
 
 FP8_PATH_RTOL = 2.0 ** -10 + 1e-5
 
 
-@pytest.mark.parametrize("kind,rtol", [("fp8", compare.FP32_RTOL), ("fp8_matrix_core", FP8_PATH_RTOL)])
+@pytest.mark.parametrize("kind,rtol", [("fp8", compare.FP32_RTOL), ("fp8_unfused", compare.FP32_RTOL),
+                                       ("fp8_matrix_core", FP8_PATH_RTOL)])
 def test_layer_stages(run, kind, rtol):
     r = run[kind]
     tr, lay = r["trace"], r["lay"]
@@ -119,7 +127,7 @@ def test_layer_chained_output(run):
     assert rel < 8e-2, rel
 
 
-@pytest.mark.parametrize("kind", ["fp8", "fp8_matrix_core"])
+@pytest.mark.parametrize("kind", ["fp8", "fp8_unfused", "fp8_matrix_core"])
 def test_layer_backward_against_bf16_layer(run, kind):
     import torch
     f, b = run[kind], run["bf16"]
@@ -130,3 +138,7 @@ def test_layer_backward_against_bf16_layer(run, kind):
         assert gf.dtype == torch.float32 and torch.isfinite(gf).all()
         c = _cos(gf, gb)
         assert c > 0.99, (i, c)
+    for i, (nf, nb) in enumerate(zip(f["norms"], b["norms"])):   # RMSNorm gains
+        assert nf is not None and torch.isfinite(nf).all()
+        c = _cos(nf, nb)
+        assert c > 0.99, ("norm", i, c)

@@ -85,3 +85,81 @@ def test_fp8_linear_weight_cache_follows_updates(torch_mod):
     assert lin.weight_quantisations == 2
     assert torch.equal(y0, y1)
     assert torch.equal(y2.float(), (2.0 * y0.float()).to(torch.bfloat16).float())
+
+
+def _rel(a, b):
+    a, b = a.double(), b.double()
+    return float((a - b).norm() / b.norm())
+
+
+def test_fused_rmsnorm_linear(torch_mod):
+    """forward_rmsnorm: forward bit-for-bit the oracle's fused RMSNorm value
+    through the FP8 GEMM (acceptance rule as above); backward against the
+    unfused composition F.rms_norm -> Fp8Linear (same FP8 data gradient, the
+    RMSNorm backward by PyTorch autograd)."""
+    torch = torch_mod
+    import torch.nn.functional as F
+    from blockwise_fp8_linear_quant_amd.linear import Fp8Linear
+    from oracle import fused
+    M, K, N = 300, 256, 384
+    xb = W.normal_bf16((M, K), 1.0, W.seed_for(2, 20, "qkv", "x"))
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(2, 20, "qkv", "w"))
+    dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(2, 20, "qkv", "dy"))
+    gam = (np.random.default_rng(5).standard_normal(K) * 0.1 + 1.0).astype(np.float32)
+    gb = W.f32_to_bf16_bits(gam)
+    gamma = torch.from_numpy(gb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    dy = dev_bf16(dyb).contiguous()
+    say("fused rmsnorm linear", M, K, N)
+    lin_f = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous())
+    x1, g1 = dev_bf16(xb).contiguous().requires_grad_(True), gamma.clone().requires_grad_(True)
+    y1 = lin_f.forward_rmsnorm(x1, g1, 1e-6)
+    y1.backward(dy)
+    lin_u = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous())
+    x2, g2 = dev_bf16(xb).contiguous().requires_grad_(True), gamma.clone().requires_grad_(True)
+    y2 = lin_u(F.rms_norm(x2, (K,), g2, 1e-6))
+    y2.backward(dy)
+    torch.cuda.synchronize()
+    hb, _ = fused.rmsnorm_bf16(xb, gb, 1e-6)
+    hq, sh = quant.quant_1x128_rows(hb)
+    wq, sw = quant.quant_128x128(wb)
+    yy, bnd = gemm.fwd(hq, sh, wq, sw)
+    ok, rep = compare.check_bf16(host(y1.detach()), yy, bnd)
+    assert ok, ("fused rmsnorm forward", rep)
+    assert _rel(x1.grad, x2.grad) < 2e-2, _rel(x1.grad, x2.grad)
+    assert _rel(g1.grad, g2.grad) < 2e-2, _rel(g1.grad, g2.grad)
+    assert _rel(lin_f.weight.main_grad, lin_u.weight.main_grad) < 2e-2
+
+
+def test_fused_swiglu_linear(torch_mod):
+    """forward_swiglu: forward against the oracle's fused SwiGLU value through
+    the FP8 GEMM; backward against F.silu(gate) * up -> Fp8Linear."""
+    torch = torch_mod
+    import torch.nn.functional as F
+    from blockwise_fp8_linear_quant_amd.linear import Fp8Linear
+    from oracle import fused
+    M, K, N = 300, 256, 384
+    gb_ = W.normal_bf16((M, K), 1.0, W.seed_for(2, 21, "down", "x"))
+    ub_ = W.normal_bf16((M, K), 1.0, W.seed_for(2, 21, "down", "dy"))
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(2, 21, "down", "w"))
+    dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(2, 22, "down", "dy"))
+    gub = np.concatenate([gb_, ub_], axis=1)
+    dy = dev_bf16(dyb).contiguous()
+    say("fused swiglu linear", M, K, N)
+    lin_f = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous())
+    gu1 = dev_bf16(gub).contiguous().requires_grad_(True)
+    y1 = lin_f.forward_swiglu(gu1)
+    y1.backward(dy)
+    lin_u = Fp8Linear(K, N, weight=dev_bf16(wb).contiguous())
+    gu2 = dev_bf16(gub).contiguous().requires_grad_(True)
+    g, u = gu2.split([K, K], dim=1)
+    y2 = lin_u(F.silu(g) * u)
+    y2.backward(dy)
+    torch.cuda.synchronize()
+    hb = fused.swiglu_bf16(gb_, ub_)
+    hq, sh = quant.quant_1x128_rows(hb)
+    wq, sw = quant.quant_128x128(wb)
+    yy, bnd = gemm.fwd(hq, sh, wq, sw)
+    ok, rep = compare.check_bf16(host(y1.detach()), yy, bnd)
+    assert ok, ("fused swiglu forward", rep)
+    assert _rel(gu1.grad, gu2.grad) < 2e-2, _rel(gu1.grad, gu2.grad)
+    assert _rel(lin_f.weight.main_grad, lin_u.weight.main_grad) < 2e-2
