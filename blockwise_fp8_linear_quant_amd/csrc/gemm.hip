@@ -55,7 +55,6 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 constexpr int BK = 128;
-constexpr int kGroupM = 8;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained; gfx9
@@ -89,16 +88,25 @@ __device__ __forceinline__ v8h cvt8(uint32_t w0, uint32_t w1) {
   return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Tile-rows per group of the launch order.  Each XCD fetches, round by round,
+// the A row panels and B column panels of the tiles it runs at once (its 4 MB
+// L2 keeps nothing from one round for the next), so a round's r x c tiles
+// cost r * BM + c * BN rows of operand: with 32 tiles per XCD that is least
+// at 4 x 8 for 256 x 128 tiles and 8 x 8 for 128 x 128 tiles (two per CU).
+template <int BM>
+constexpr int group_rows() { return BM == 256 ? 4 : 8; }
+
+template <int GM>
 __device__ __forceinline__ void map_tile(int pid, int nblocks, int tilesM, int tilesN, int& tm, int& tn) {
   // Workgroup pid runs on XCD pid % 8; give each XCD a contiguous logical range.
   const int q = nblocks / 8, r = nblocks % 8;
   const int xcd = pid % 8, local = pid / 8;
   const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-  // Grouped order: kGroupM tile-rows at a time, walking down columns.
-  const int per_group = kGroupM * tilesN;
+  // Grouped order: GM tile-rows at a time, walking down columns.
+  const int per_group = GM * tilesN;
   const int gid = logical / per_group;
-  const int first_m = gid * kGroupM;
-  const int gm = min(tilesM - first_m, kGroupM);
+  const int first_m = gid * GM;
+  const int gm = min(tilesM - first_m, GM);
   const int in_group = logical - gid * per_group;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   int tm, tn;
-  map_tile(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  map_tile<group_rows<BM>()>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int nLB = (int)(L / BK);
@@ -437,7 +445,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   int tm, tn;
-  map_tile(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  map_tile<group_rows<BM>()>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int nLB = (int)(L / BK);
@@ -597,7 +605,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void bf16_ge
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   int tm, tn;
-  map_tile(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  map_tile<group_rows<BM>()>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   const int wm = wave / WGN, wn = wave % WGN;
   const int nLB = (int)(L / BK16);

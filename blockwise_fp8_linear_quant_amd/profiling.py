@@ -29,6 +29,7 @@ Usage (on the CPU, after the profiler runs):
 import argparse
 import csv
 import hashlib
+import json
 import os
 import re
 
@@ -64,7 +65,7 @@ def short_name(name):
     return name.replace("fp8blk::(anonymous namespace)::", "")
 
 
-def stats_summary(stats_csv, command, steps=None):
+def stats_summary(stats_csv, command, bench_json=None):
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"command: {command}", "",
              f"{'kernel':<78} {'calls':>6} {'avg_us':>9} {'total_ms':>9} {'share%':>7}"]
@@ -76,9 +77,15 @@ def stats_summary(stats_csv, command, steps=None):
     if gemm:
         calls = sum(int(r["Calls"]) for r in gemm)
         tot = sum(float(r["TotalDurationNs"]) for r in gemm)
-        lines += ["", f"{GEMM_KERNEL} (all instantiations): {calls} calls, average {tot / calls / 1e3:.2f} us"]
-        if steps:
-            lines.append(f"per step ({steps} steps incl. warmup): {tot / steps / 1e3:.1f} us")
+        avg_us = tot / calls / 1e3
+        lines += ["", f"{GEMM_KERNEL} (all instantiations): {calls} calls, average {avg_us:.2f} us"]
+        if bench_json:
+            # bench.py's own figure from the same profiled process: HIP events
+            # around the timed steps on the stream the GEMMs run on.
+            rec = json.loads(open(bench_json).read().strip().splitlines()[-1])["roofline"]
+            lines += [f"bench.py in the same run: average launch {rec['avg_launch_us']:.2f} us over "
+                      f"{rec['launches_per_step']} launches per step, {rec['achieved']:.1f} TFLOP/s",
+                      f"rocprofv3 average / bench.py average: {avg_us / rec['avg_launch_us']:.3f}"]
     return "\n".join(lines) + "\n"
 
 
@@ -238,7 +245,7 @@ def main():
     s.add_argument("stats_csv")
     s.add_argument("out")
     s.add_argument("--command", required=True)
-    s.add_argument("--steps", type=int)
+    s.add_argument("--bench-json", help="bench.py output of the profiled command")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
@@ -252,7 +259,7 @@ def main():
     c.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "stats":
-        text = stats_summary(a.stats_csv, a.command, a.steps)
+        text = stats_summary(a.stats_csv, a.command, a.bench_json)
     elif a.cmd == "traffic":
         text = traffic_summary(a.fetch_csv, a.write_csv, a.copy_bytes, a.command, a.algorithmic_bytes)
     else:
