@@ -91,6 +91,23 @@ FP8BLK_HD SetupEntry setup_entry(int m) {
   return e;
 }
 
+// The same 128 entries evaluated at compile time (binary32, round to nearest
+// even; dividing by 16 or 32 is exact, like the ldexpf of setup_entry), so a
+// kernel can copy its table instead of dividing.
+struct SetupTable {
+  SetupEntry e[128];
+};
+
+constexpr SetupTable make_setup_table() {
+  SetupTable tb{};
+  for (int m = 0; m < 128; ++m) {
+    const float t = (float)(128 + m) / 7.0f;
+    tb.e[m].s_n = m >= 96 ? t / 32.0f : t / 16.0f;
+    tb.e[m].r_n = 1.0f / tb.e[m].s_n;
+  }
+  return tb;
+}
+
 FP8BLK_HD GroupQ group_setup_bf16(float amax, const SetupEntry* tab) {
   const uint32_t b = f32_bits(amax);
   const int e = (int)(b >> 23);

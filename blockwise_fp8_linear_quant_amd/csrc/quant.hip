@@ -251,6 +251,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT) {
   __shared__ float red[4];
   __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
+  __shared__ float4 rowq[128], colq[128];   // per-group constants {s_n, r_n, k, s} of the tile
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t br = blockIdx.y, bc = blockIdx.x;
   const int c = t & 15, rb = t >> 4;
@@ -335,6 +336,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
 // of 4.  Token rows past R (up to the 128-padded length) read as zero and
 // come out as 0x00 pads in qT.
 // ---------------------------------------------------------------------------
+__device__ constexpr SetupTable kSetupTab = make_setup_table();
+
 __device__ __forceinline__ uint32_t code4_each(float a, float b, float c, float d, const GroupQ (&g)[8], int j0) {
   // Four values of one row, columns j0..j0+3, each with its own column's
   // scale.  A zero column group has s_n = r_n = 1, k = 0 and only +-0
@@ -410,12 +413,13 @@ __device__ __forceinline__ void dual_encode(
     const uint4 (&v)[8], int64_t br, int64_t bc, int64_t R, int64_t C,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
-    float (*cred)[128], const SetupEntry* stab, uint4* stage) {
+    float (*cred)[128], const SetupEntry* stab, uint4* stage, float4* rowq, float4* colq) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
   // Column maxima of this thread's 8 columns over its 8 rows, then over the
-  // 4 row blocks of the wave (lanes 16 and 32 apart), then over the waves.
+  // 4 row blocks of the wave (lanes 16 and 32 apart); after the barrier
+  // thread t < 128 combines the 4 waves' maxima of column t.
   float cm[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -442,24 +446,43 @@ __device__ __forceinline__ void dual_encode(
   }
   // LDS-only barrier, so that a fused producer's BF16 stores stay in flight.
   lds_barrier();
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    cm[j] = fmaxf(fmaxf(cred[0][c * 8 + j], cred[1][c * 8 + j]), fmaxf(cred[2][c * 8 + j], cred[3][c * 8 + j]));
+  const int tt = t & 127;
+  const float cmx = fmaxf(fmaxf(cred[0][tt], cred[1][tt]), fmaxf(cred[2][tt], cred[3][tt]));
 
-  // Column groups: scales out, constants kept; then each row is set up,
-  // encoded both ways and its row-wise codes stored.
+  // Group constants are set up once per group and shared through LDS (each
+  // thread would otherwise set up all 16 of its groups): lane c < 8 of each
+  // DPP row sets up row r0 + c (all 16 lanes hold the 8 row maxima) and
+  // stores its scale, thread t < 128 does the same for column t.
+  {
+    float m = rm[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = (c == i) ? rm[i] : m;
+    if (c < 8) {
+      const GroupQ g = group_setup_bf16(m, stab);
+      rowq[rb * 8 + c] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
+      if (FULL || r0 + c < R) s[bc * lds + r0 + c] = g.s;
+    }
+  }
+  if (t < 128) {
+    const GroupQ g = group_setup_bf16(cmx, stab);
+    colq[t] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
+    if (FULL || bc * 128 + t < C) sT[br * ldsT + bc * 128 + t] = g.s;
+  }
+  lds_barrier();
   GroupQ gc[8];
-  uint32_t cmask[2] = {0u, 0u};   // 0xFF for the bytes of non-zero column groups
+  uint32_t cmask[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    gc[j] = group_setup_bf16(cm[j], stab);
-    if (gc[j].s != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
-    if ((FULL || c0 + j < C) && rb == 0) sT[br * ldsT + c0 + j] = gc[j].s;
+    const float4 e = colq[c * 8 + j];
+    gc[j].s_n = e.x; gc[j].r_n = e.y; gc[j].k = __float_as_int(e.z); gc[j].s = e.w;
+    if (e.w != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
   }
-  uint32_t rw[8][2];           // token-dimension codes, row-major (column scales)
+  uint32_t rw[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const GroupQ g = group_setup_bf16(rm[i], stab);
+    const float4 e = rowq[rb * 8 + i];
+    GroupQ g;
+    g.s_n = e.x; g.r_n = e.y; g.k = __float_as_int(e.z); g.s = e.w;
     const uint32_t keep = (g.s == 0.0f) ? 0u : 0xffffffffu;
     const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
     const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
@@ -468,10 +491,8 @@ __device__ __forceinline__ void dual_encode(
     const int64_t r = r0 + i;
     if (FULL) {
       *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
-      if (c == 0) s[bc * lds + r] = g.s;
     } else if (r < R && c0 < C) {
       store8(q + r * ldq + c0, c0, C, lo, hi);
-      if (c == 0) s[bc * lds + r] = g.s;
     }
   }
   // Token-dimension codes: 4x4 byte transposes into words of 4 tokens each.
@@ -503,8 +524,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   __shared__ float cred[4][128];
   __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
   __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
+  __shared__ float4 rowq[128], colq[128];   // per-group constants {s_n, r_n, k, s} of the tile
   const int t = threadIdx.x;
-  if (t < 128) stab[t] = setup_entry(t);
+  if (t < 128) stab[t] = kSetupTab.e[t];
   const int64_t br = blockIdx.y, bc = blockIdx.x;
   const bool full = (br + 1) * 128 <= R && (bc + 1) * 128 <= C;
   const int c = t & 15, rb = t >> 4;
@@ -536,8 +558,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       }
     }
   }
-  if (full) dual_encode<true>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage);
-  else dual_encode<false>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage);
+  if (full) dual_encode<true>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage, rowq, colq);
+  else dual_encode<false>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage, rowq, colq);
 }
 
 // RMSNorm statistics: rstd[r] = 1 / sqrt(mean_c x[r, c]^2 + eps) in binary32,

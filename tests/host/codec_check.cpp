@@ -46,11 +46,20 @@ extern "C" int codec_quotient_scan(uint32_t amax_lo, uint32_t amax_hi, uint64_t*
 }
 
 // Table-driven group setup against group_setup for every BF16 magnitude:
-// returns the number of maxima whose four constants differ in any bit.
+// returns the number of maxima whose four constants differ in any bit.  The
+// table is the compile-time one the kernels copy; its entries must also equal
+// setup_entry's, evaluated at run time.
 extern "C" int codec_setup_table_scan(void) {
-  fp8blk::SetupEntry tab[128];
-  for (int m = 0; m < 128; ++m) tab[m] = fp8blk::setup_entry(m);
+  static constexpr fp8blk::SetupTable kTab = fp8blk::make_setup_table();
+  const fp8blk::SetupEntry* tab = kTab.e;
   int bad = 0;
+  for (int m = 0; m < 128; ++m) {
+    const fp8blk::SetupEntry r = fp8blk::setup_entry(m);
+    if (fp8blk::f32_bits(r.s_n) != fp8blk::f32_bits(tab[m].s_n) || fp8blk::f32_bits(r.r_n) != fp8blk::f32_bits(tab[m].r_n)) {
+      std::printf("TABLE MISMATCH m=%d\n", m);
+      ++bad;
+    }
+  }
   for (uint32_t ab = 0; ab < 0x7f80; ++ab) {
     const float amax = fp8blk::bf16_to_f32(ab);
     const fp8blk::GroupQ a = fp8blk::group_setup(amax), b = fp8blk::group_setup_bf16(amax, tab);
