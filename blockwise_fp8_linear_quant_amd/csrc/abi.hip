@@ -12,6 +12,10 @@ using namespace fp8blk;
 // Per-device cache of "is gfx950" (0 = unknown, 1 = yes, 2 = no).  Benign race:
 // every writer stores the same value.
 constexpr int kMaxDevices = 64;
+// Row strides (bytes) of GEMM operands: a 256-row tile spans less than 2^31.
+constexpr int64_t kMaxGemmLd = (int64_t)1 << 23;
+// Workgroups of a one-dimensional grid.
+constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 1;
 int g_arch_ok[kMaxDevices];
 
 bool device_ok() {
@@ -24,6 +28,9 @@ bool device_ok() {
   if (dev < kMaxDevices) g_arch_ok[dev] = ok ? 1 : 2;
   return ok;
 }
+
+// Workgroups of a quantiser that gives each 128 x 128 tile one workgroup.
+inline int64_t tiles128(int64_t rows, int64_t cols) { return (rows + 127) / 128 * ((cols + 127) / 128); }
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -46,8 +53,10 @@ int check_gemm(int64_t I, int64_t J, int64_t L, const void* A, int64_t lda, cons
   if (L == 0) return 0;
   if (A == nullptr || B == nullptr || SA == nullptr || SB == nullptr) return FP8BLK_INVALID_ARG;
   if (lda < L || ldb < L || ldsa < L_valid_rows_sa) return FP8BLK_INVALID_ARG;
-  // The kernels address operand rows with 32-bit byte offsets.
-  if (I * lda >= (int64_t)1 << 31 || J * ldb >= (int64_t)1 << 31) return FP8BLK_UNSUPPORTED_SHAPE;
+  // The kernels address the rows of a tile with 32-bit byte offsets from the
+  // tile's first row, and number the tiles in one grid dimension.
+  if (lda >= kMaxGemmLd || ldb >= kMaxGemmLd) return FP8BLK_UNSUPPORTED_SHAPE;
+  if ((I + 127) / 128 * (J / 128) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
   if (sb_rows && ldsb < J) return FP8BLK_INVALID_ARG;
   if (!al16(A) || !al16(B) || lda % 16 != 0 || ldb % 16 != 0) return FP8BLK_MISALIGNED;
   if (!al16(SA) || ldsa % 4 != 0) return FP8BLK_MISALIGNED;
@@ -72,6 +81,11 @@ int fp8_quant_1x128(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x
     const int64_t mpad = (rows + 127) / 128 * 128;
     if (ld_q < mpad || ld_s < cols) return FP8BLK_INVALID_ARG;
   }
+  // Grids: row blocks x column groups (at most 65535) for the row-wise
+  // kernel, one dimension of (token group, 256-feature block) otherwise.
+  if (transpose_out == 0 ? ((cols + 127) / 128 > 65535 || (rows + 31) / 32 >= kMaxGrid)
+                         : (rows + 127) / 128 * ((cols + 255) / 256) >= kMaxGrid)
+    return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(x_bf16) || ld_x % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al4(scales)) return FP8BLK_MISALIGNED;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -91,6 +105,7 @@ int fp8_quant_1x128_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t
     return FP8BLK_INVALID_ARG;
   const int64_t mpad = (rows + 127) / 128 * 128;
   if (ld_x < cols || ld_q < cols || ld_s < rows || ld_qT < mpad || ld_sT < cols) return FP8BLK_INVALID_ARG;
+  if (tiles128(rows, cols) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(x_bf16) || ld_x % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al16(qT) || ld_qT % 16 != 0 ||
       !al4(scales) || !al4(scalesT))
     return FP8BLK_MISALIGNED;
@@ -109,6 +124,7 @@ int check_dual_outputs(int64_t rows, int64_t cols, const uint8_t* q, int64_t ld_
   const int64_t mpad = (rows + 127) / 128 * 128;
   if (ld_q < cols || ld_s < rows || ld_qT < mpad || ld_sT < cols) return FP8BLK_INVALID_ARG;
   if (bf16_out != nullptr && ld_out < cols) return FP8BLK_INVALID_ARG;
+  if (tiles128(rows, cols) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(q) || ld_q % 16 != 0 || !al16(qT) || ld_qT % 16 != 0 || !al4(scales) || !al4(scalesT)) return FP8BLK_MISALIGNED;
   if (bf16_out != nullptr && (!al16(bf16_out) || ld_out % 8 != 0)) return FP8BLK_MISALIGNED;
   return FP8BLK_OK;
@@ -158,6 +174,7 @@ int fp8_quant_128x128(const void* w_bf16, int64_t rows, int64_t cols, int64_t ld
   if (rows == 0 || cols == 0) return FP8BLK_OK;
   if (w_bf16 == nullptr || q == nullptr || scales == nullptr) return FP8BLK_INVALID_ARG;
   if (ld_w < cols || ld_q < cols || (qT != nullptr && ld_qT < rows)) return FP8BLK_INVALID_ARG;
+  if (tiles128(rows, cols) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(w_bf16) || ld_w % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al4(scales)) return FP8BLK_MISALIGNED;
   if (qT != nullptr && (!al16(qT) || ld_qT % 16 != 0 || !al4(scalesT))) return FP8BLK_MISALIGNED;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
@@ -262,8 +279,9 @@ int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,
   if (!al16(c) || ld_c % (out == OUT_BF16 ? 8 : 4) != 0) return FP8BLK_MISALIGNED;
   if (K > 0) {
     if (a == nullptr || b == nullptr || ld_a < K || ld_b < K) return FP8BLK_INVALID_ARG;
+    if (ld_a * 2 >= kMaxGemmLd || ld_b * 2 >= kMaxGemmLd) return FP8BLK_UNSUPPORTED_SHAPE;
+    if ((M + 127) / 128 * (N / 128) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
     if (!al16(a) || !al16(b) || ld_a % 8 != 0 || ld_b % 8 != 0) return FP8BLK_MISALIGNED;
-    if (M * ld_a * 2 >= (int64_t)1 << 31 || N * ld_b * 2 >= (int64_t)1 << 31) return FP8BLK_UNSUPPORTED_SHAPE;
   }
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
   launch_bf16_gemm(static_cast<const uint16_t*>(a), ld_a, static_cast<const uint16_t*>(b), ld_b, M, N, K, c, ld_c,

@@ -162,9 +162,10 @@ __device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_
 // Direct-to-LDS staging.  A tile of ROWS rows x 128 bytes moves with ROWS/8
 // wave instructions of 1 KB; lane L of instruction `blk` writes LDS bytes
 // [16L, 16L+16) of its 1 KB, i.e. tile row r = 8 blk + L/8, slot L%8, which
-// must hold global chunk (L%8) ^ swz_key(r) of that row.  The per-lane byte offsets of
-// the source rows are loop invariant (computed once, 32-bit: every operand
-// here is below 2 GiB); per scale block only the wave-uniform base pointer
+// must hold global chunk (L%8) ^ swz_key(r) of that row.  The per-lane byte
+// offsets are relative to the tile's first row and loop invariant (computed
+// once; 32-bit, which holds for any row stride below 2^23 bytes whatever the
+// operand's size); per scale block only the wave-uniform 64-bit base pointer
 // moves, so each load is one instruction with no address arithmetic.  Rows
 // past the last valid row are clamped to it; they only feed output rows that
 // are never stored.
@@ -179,10 +180,10 @@ struct TileStager {
       const int trow = 8 * (NW * u + wave) + (lane >> 3);   // row within the tile
       int64_t row = r0 + trow;
       row = row < rmax ? row : rmax;
-      off[u] = (uint32_t)(row * ld) + (uint32_t)(((lane & 7) ^ swz_key(trow)) * 16);
+      off[u] = (uint32_t)((row - r0) * ld) + (uint32_t)(((lane & 7) ^ swz_key(trow)) * 16);
     }
   }
-  // base: G + lb * 128 (wave-uniform); dst: the tile in LDS.
+  // base: G + r0 * ld + lb * 128 (wave-uniform); dst: the tile in LDS.
   __device__ __forceinline__ void issue(const uint8_t* base, uint8_t* dst, int wave) const {
     const uint32_t l0 = lds_addr(dst) + wave * 1024;
 #pragma unroll
@@ -200,9 +201,9 @@ struct ScaleStager {
   __device__ __forceinline__ void init(int64_t r0, int64_t rmax, int wave, int lane) {
     int64_t r = r0 + kPerWave * wave + (lane < kPerWave ? lane : 0);
     r = r < rmax ? r : rmax;
-    off = (uint32_t)r * 4u;
+    off = (uint32_t)(r - r0) * 4u;   // relative to the tile's first row
   }
-  // base: SC + lb * ld (wave-uniform).
+  // base: SC + lb * ld + r0 (wave-uniform).
   __device__ __forceinline__ void issue(const float* base, float* dst, int wave, int lane) const {
     const uint32_t l0 = lds_addr(dst + kPerWave * wave);
     if (lane < kPerWave) dma_b32(base, off, l0);
@@ -274,10 +275,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   ssa.init(i0, I - 1, wave, lane);
   ssb.init(j0, j0 + BN - 1, wave, lane);
   auto stage_all = [&](int lb, uint8_t* buf) {
-    sta.issue(A + (int64_t)lb * BK, buf, wave);
-    stb.issue(B + (int64_t)lb * BK, buf + BM * BK, wave);
-    ssa.issue(SA + (int64_t)lb * ldsa, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
-    if (SB_MODE == SB_ROWS) ssb.issue(SB + (int64_t)lb * ldsb, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
+    sta.issue(A + i0 * lda + (int64_t)lb * BK, buf, wave);
+    stb.issue(B + j0 * ldb + (int64_t)lb * BK, buf + BM * BK, wave);
+    ssa.issue(SA + (int64_t)lb * ldsa + i0, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
+    if (SB_MODE == SB_ROWS)
+      ssb.issue(SB + (int64_t)lb * ldsb + j0, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
   };
 
   uint4 qa[2][MT], qb[2][NT];   // raw codes of two K slices (software pipeline)
@@ -468,10 +470,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   ssa.init(i0, last_row, wave, lane);
   ssb.init(j0, j0 + BN - 1, wave, lane);
   auto stage_all = [&](int lb, uint8_t* buf) {
-    sta.issue(A + (int64_t)lb * BK, buf, wave);
-    stb.issue(B + (int64_t)lb * BK, buf + BM * BK, wave);
-    ssa.issue(SA + (int64_t)lb * ldsa, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
-    if (SB_MODE == SB_ROWS) ssb.issue(SB + (int64_t)lb * ldsb, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
+    sta.issue(A + i0 * lda + (int64_t)lb * BK, buf, wave);
+    stb.issue(B + j0 * ldb + (int64_t)lb * BK, buf + BM * BK, wave);
+    ssa.issue(SA + (int64_t)lb * ldsa + i0, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
+    if (SB_MODE == SB_ROWS)
+      ssb.issue(SB + (int64_t)lb * ldsb + j0, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
   };
 
   {
@@ -627,8 +630,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void bf16_ge
   sta.init(lda * 2, i0, I - 1, wave, lane);
   stb.init(ldb * 2, j0, j0 + BN - 1, wave, lane);
   auto stage_all = [&](int lb, uint8_t* buf) {
-    sta.issue(Ab + (int64_t)lb * BK, buf, wave);
-    stb.issue(Bb + (int64_t)lb * BK, buf + BM * BK, wave);
+    sta.issue(Ab + i0 * lda * 2 + (int64_t)lb * BK, buf, wave);
+    stb.issue(Bb + j0 * ldb * 2 + (int64_t)lb * BK, buf + BM * BK, wave);
   };
   uint4 qa[2][MT], qb[2][NT];
   auto load_slice = [&](const uint8_t* buf, int c, int slot) {

@@ -200,10 +200,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t C, int64_t ldx,
-    uint8_t* __restrict__ qT, int64_t ldq, float* __restrict__ s, int64_t lds) {
+    uint8_t* __restrict__ qT, int64_t ldq, float* __restrict__ s, int64_t lds, uint32_t nfb) {
   const int lane = threadIdx.x & 63;
-  const int64_t tg = blockIdx.y;
-  const int64_t f0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64 + (lane & 7) * 8;
+  // One-dimensional grid (token groups can exceed the 65535 limit of y):
+  // workgroup (token group, feature block) in feature-fastest order.
+  const int64_t tg = blockIdx.x / nfb, fb = blockIdx.x % nfb;
+  const int64_t f0 = (fb * 4 + (threadIdx.x >> 6)) * 64 + (lane & 7) * 8;
   const int b = lane >> 3;
   const int64_t t0 = tg * 128 + b * 16;
 
@@ -248,12 +250,11 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
 __global__ __launch_bounds__(256) void quant_blocks_kernel(
     const uint16_t* __restrict__ w, int64_t R, int64_t C, int64_t ldw,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
-    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT) {
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, uint32_t nbc) {
   __shared__ float red[4];
   __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
-  __shared__ float4 rowq[128], colq[128];   // per-group constants {s_n, r_n, k, s} of the tile
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t br = blockIdx.y, bc = blockIdx.x;
+  const int64_t br = blockIdx.x / nbc, bc = blockIdx.x % nbc;   // one-dimensional grid, column tiles fastest
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
 
@@ -511,8 +512,9 @@ __device__ __forceinline__ void dual_encode(
   store_codes_transposed(cw, stage, qT + bc * 128 * ldqT + br * 128, ldqT, FULL ? 128 : C - bc * 128);
 }
 
-// The dual quantiser over any element source, one 128x128 tile (blockIdx.y,
-// blockIdx.x) per workgroup; interior tiles take unguarded loads and stores.
+// The dual quantiser over any element source, one 128x128 tile per workgroup
+// (row tile blockIdx.x / nbc, column tile blockIdx.x % nbc); interior tiles
+// take unguarded loads and stores.
 // `hout` (optional, BF16 [R, ld_h]) receives the source values themselves --
 // for a fused producer, the BF16 tensor it would otherwise have written.
 template <class Src>
@@ -520,14 +522,14 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
     Src src, int64_t R, int64_t C,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
-    uint16_t* __restrict__ hout, int64_t ldh) {
+    uint16_t* __restrict__ hout, int64_t ldh, uint32_t nbc) {
   __shared__ float cred[4][128];
   __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
   __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
   __shared__ float4 rowq[128], colq[128];   // per-group constants {s_n, r_n, k, s} of the tile
   const int t = threadIdx.x;
   if (t < 128) stab[t] = kSetupTab.e[t];
-  const int64_t br = blockIdx.y, bc = blockIdx.x;
+  const int64_t br = blockIdx.x / nbc, bc = blockIdx.x % nbc;   // one-dimensional grid, column tiles fastest
   const bool full = (br + 1) * 128 <= R && (bc + 1) * 128 <= C;
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
@@ -595,32 +597,36 @@ void launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
 
 void launch_quant_tokens(const uint16_t* x, int64_t M, int64_t C, int64_t ldx,
                          uint8_t* qT, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
-  dim3 grid((unsigned)((C + 255) / 256), (unsigned)((M + 127) / 128));
-  hipLaunchKernelGGL(quant_tokens_kernel, grid, dim3(256), 0, st, x, M, C, ldx, qT, ldq, s, lds);
+  const uint32_t nfb = (uint32_t)((C + 255) / 256);
+  const dim3 grid((unsigned)(nfb * ((M + 127) / 128)));
+  hipLaunchKernelGGL(quant_tokens_kernel, grid, dim3(256), 0, st, x, M, C, ldx, qT, ldq, s, lds, nfb);
 }
 
 void launch_quant_blocks(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
                          uint8_t* q, int64_t ldq, float* s,
                          uint8_t* qT, int64_t ldqT, float* sT, hipStream_t st) {
-  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
-  hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, st, w, R, C, ldw, q, ldq, s, qT, ldqT, sT);
+  const uint32_t nbc = (uint32_t)((C + 127) / 128);
+  const dim3 grid((unsigned)(nbc * ((R + 127) / 128)));
+  hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, st, w, R, C, ldw, q, ldq, s, qT, ldqT, sT, nbc);
 }
 
 void launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                        uint8_t* q, int64_t ldq, float* s, int64_t lds,
                        uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st) {
-  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
+  const uint32_t nbc = (uint32_t)((C + 127) / 128);
+  const dim3 grid((unsigned)(nbc * ((R + 127) / 128)));
   hipLaunchKernelGGL(quant_dual_kernel<SrcPlain>, grid, dim3(256), 0, st, SrcPlain{x, ldx}, R, C, q, ldq, s, lds,
-                     qT, ldqT, sT, ldsT, (uint16_t*)nullptr, (int64_t)0);
+                     qT, ldqT, sT, ldsT, (uint16_t*)nullptr, (int64_t)0, nbc);
 }
 
 void launch_swiglu_quant_dual(const uint16_t* g, int64_t ldg, const uint16_t* u, int64_t ldu, int64_t R, int64_t C,
                               uint8_t* q, int64_t ldq, float* s, int64_t lds,
                               uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                               uint16_t* h, int64_t ldh, hipStream_t st) {
-  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
+  const uint32_t nbc = (uint32_t)((C + 127) / 128);
+  const dim3 grid((unsigned)(nbc * ((R + 127) / 128)));
   hipLaunchKernelGGL(quant_dual_kernel<SrcSwiGLU>, grid, dim3(256), 0, st, SrcSwiGLU{g, ldg, u, ldu}, R, C,
-                     q, ldq, s, lds, qT, ldqT, sT, ldsT, h, ldh);
+                     q, ldq, s, lds, qT, ldqT, sT, ldsT, h, ldh, nbc);
 }
 
 void launch_rmsnorm_quant_dual(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t R, int64_t C,
@@ -628,9 +634,10 @@ void launch_rmsnorm_quant_dual(const uint16_t* x, int64_t ldx, const uint16_t* g
                                uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                                uint16_t* y, int64_t ldy, hipStream_t st) {
   hipLaunchKernelGGL(rmsnorm_rstd_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, x, R, C, ldx, eps, rstd);
-  dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128));
+  const uint32_t nbc = (uint32_t)((C + 127) / 128);
+  const dim3 grid((unsigned)(nbc * ((R + 127) / 128)));
   hipLaunchKernelGGL(quant_dual_kernel<SrcRMSNorm>, grid, dim3(256), 0, st, SrcRMSNorm{x, ldx, rstd, gamma}, R, C,
-                     q, ldq, s, lds, qT, ldqT, sT, ldsT, y, ldy);
+                     q, ldq, s, lds, qT, ldqT, sT, ldsT, y, ldy, nbc);
 }
 
 void launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t st) {

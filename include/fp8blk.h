@@ -44,6 +44,13 @@
  *     a multiple of 4, BF16 outputs ld a multiple of 8.
  *   - Calls on one stream are ordered; calls on different streams that write
  *     the same buffers race.
+ *   - Size limits (FP8BLK_UNSUPPORTED_SHAPE beyond them): GEMM operand rows
+ *     shorter than 2^23 bytes (ld_* of the code and BF16 operands), and fewer
+ *     than 2^31 - 1 workgroups: 128 x 128 output tiles for the GEMMs and the
+ *     128 x 128 quantisers, (128 tokens x 256 features) blocks for the token
+ *     quantiser, 32-row blocks for the row-wise one, whose column count is
+ *     also limited to 65535 x 128.  Total operand size is otherwise not
+ *     limited (offsets are 64-bit above the tile level).
  */
 #ifndef FP8BLK_H
 #define FP8BLK_H
@@ -58,7 +65,7 @@ extern "C" {
 typedef enum fp8blk_status {
   FP8BLK_OK = 0,
   FP8BLK_INVALID_ARG = 1,        /* null pointer, negative size, ld too small, bad enum */
-  FP8BLK_UNSUPPORTED_SHAPE = 2,  /* GEMM: N or K not a multiple of 128, or an operand of 2 GiB or more */
+  FP8BLK_UNSUPPORTED_SHAPE = 2,  /* GEMM: N or K not a multiple of 128, or a size limit below */
   FP8BLK_MISALIGNED = 3,         /* pointer or leading dimension alignment */
   FP8BLK_WORKSPACE_TOO_SMALL = 4,
   FP8BLK_DEVICE_UNSUPPORTED = 5, /* current device is not gfx950 */
@@ -249,8 +256,8 @@ int fp8_block_gemm(int op, int flags, const uint8_t* a, int64_t ld_a, const floa
  * aligned, ld_a and ld_b multiples of 8 elements; c [M, ld_c >= N], FP32 or
  * BF16 (c_dtype, rounded to nearest even), 16-byte aligned, ld_c a multiple
  * of 4 (FP32) or 8 (BF16).  N must be a multiple of 128 and K of 64 (else
- * FP8BLK_UNSUPPORTED_SHAPE); M is arbitrary; K = 0 writes zeros.  Row offsets
- * (M * ld_a and N * ld_b, in bytes) must stay below 2 GiB.
+ * FP8BLK_UNSUPPORTED_SHAPE); M is arbitrary; K = 0 writes zeros.  Rows of a
+ * and b must be shorter than 2^23 bytes (ld_a, ld_b < 2^22 elements).
  */
 int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,
                  int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, void* stream);

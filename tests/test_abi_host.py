@@ -90,6 +90,38 @@ def test_validation_happens_before_launch():
     assert lib.fp8_e4m3_encode(P, P, -1, None) == 1
 
 
+def test_size_limits_are_per_row_and_per_grid():
+    """Operands past 2 GiB and more than 65535 token groups pass the size checks.
+
+    Each such call is stopped by a deliberately misaligned pointer, which is
+    checked after the sizes: status 3 (MISALIGNED) instead of 2
+    (UNSUPPORTED_SHAPE) shows the sizes passed, and nothing is launched.
+    """
+    lib = _lib()
+    P = ctypes.c_void_p(16)
+    Q = ctypes.c_void_p(17)
+    M = (1 << 20) + 300                     # 2^20 + 300 rows of 2048 codes: 2.15 GB
+    Mp = -(-M // 128) * 128
+    assert lib.fp8_block_gemm_fwd(Q, 2048, P, M, P, 2048, P, M, 256, 2048, P, 256, 1, None, 0, None) == 3
+    assert lib.fp8_block_gemm_wgrad(Q, Mp, P, 2048, P, Mp, P, 256, M, 2048, 256, P, 256, 0, None, 0, None) == 3
+    T = 65536 * 128 + 300                   # 65539 token groups
+    Tp = -(-T // 128) * 128
+    assert lib.fp8_quant_1x128_dual(Q, T, 128, 128, P, 128, P, T, P, Tp, P, 128, None) == 3
+    assert lib.fp8_quant_1x128(Q, T, 128, 128, 1, P, Tp, P, 128, None) == 3
+    assert lib.fp8_quant_128x128(Q, T, 128, 128, P, 128, P, None, 0, None, None) == 3
+    assert lib.bf16_gemm_nt(Q, 2048, P, 2048, M, 256, 2048, P, 256, 0, None) == 3
+    # the limits themselves: a row of 2^23 bytes, a row-wise grid of 65536
+    # column groups, more than 2^31 - 1 workgroups
+    assert lib.fp8_block_gemm_fwd(P, 1 << 23, P, 16, P, 2048, P, 16, 256, 2048, P, 256, 1, None, 0, None) == 2
+    assert lib.fp8_block_gemm_wgrad(P, 1 << 23, P, 256, P, 1 << 23, P, 256, 1 << 23, 256, 256, P, 256, 0, None, 0,
+                                    None) == 2
+    assert lib.bf16_gemm_nt(P, 1 << 22, P, 2048, 16, 256, 2048, P, 256, 0, None) == 2
+    big = 1 << 23
+    assert lib.fp8_quant_1x128(P, 4, big, big, 0, P, big, P, 4, None) == 2
+    assert lib.fp8_quant_1x128_dual(P, big, big, big, P, big, P, big, P, big, P, big, None) == 2
+    assert lib.fp8_quant_128x128(P, big, big, big, P, big, P, None, 0, None, None) == 2
+
+
 def test_binding_raises_without_library(tmp_path):
     from blockwise_fp8_linear_quant_amd import _lib as L
     saved = L._lib
