@@ -453,20 +453,23 @@ __device__ __forceinline__ void dual_encode(
   // Group constants are set up once per group and shared through LDS (each
   // thread would otherwise set up all 16 of its groups): lane c < 8 of each
   // DPP row sets up row r0 + c (all 16 lanes hold the 8 row maxima) and
-  // stores its scale, thread t < 128 does the same for column t.
+  // stores its scale, thread t < 128 does the same for column t.  Both tables
+  // are index-major (rowq[i][rb], colq[j][c]): the 16 lanes of a read either
+  // share one row entry or take 16 consecutive column entries, free of bank
+  // conflicts.
   {
     float m = rm[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) m = (c == i) ? rm[i] : m;
     if (c < 8) {
       const GroupQ g = group_setup_bf16(m, stab);
-      rowq[rb * 8 + c] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
+      rowq[c * 16 + rb] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
       if (FULL || r0 + c < R) s[bc * lds + r0 + c] = g.s;
     }
   }
   if (t < 128) {
     const GroupQ g = group_setup_bf16(cmx, stab);
-    colq[t] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
+    colq[(t & 7) * 16 + (t >> 3)] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
     if (FULL || bc * 128 + t < C) sT[br * ldsT + bc * 128 + t] = g.s;
   }
   lds_barrier();
@@ -474,14 +477,14 @@ __device__ __forceinline__ void dual_encode(
   uint32_t cmask[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float4 e = colq[c * 8 + j];
+    const float4 e = colq[j * 16 + c];
     gc[j].s_n = e.x; gc[j].r_n = e.y; gc[j].k = __float_as_int(e.z); gc[j].s = e.w;
     if (e.w != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
   }
   uint32_t rw[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float4 e = rowq[rb * 8 + i];
+    const float4 e = rowq[i * 16 + rb];
     GroupQ g;
     g.s_n = e.x; g.r_n = e.y; g.k = __float_as_int(e.z); g.s = e.w;
     const uint32_t keep = (g.s == 0.0f) ? 0u : 0xffffffffu;
