@@ -6,6 +6,8 @@ Closed forms and special cases that a wiring slip would break:
 * attention: the first query sees only the first key (its output is that
   value row); equal keys give the running mean of the values; query heads
   2h and 2h+1 read key/value head h (a distinct value per head shows it);
+  scores are scaled by 1/sqrt(128): scores 0 and sqrt(128) ln 3 give the
+  weights 1/4 and 3/4 exactly;
 * RMSNorm of a constant row is +-1; silu(gate) (up = 1) equals the pinned
   fused reference, and the layer rounds it to BF16 before multiplying by up;
 * the whole layer with zero output projections is the identity (residuals),
@@ -65,6 +67,24 @@ def test_attention_head_sharing():
     out = out.reshape(s, 16, 128)
     for h in range(16):
         assert np.all(out[:, h] == h // 2 + 1.0)
+
+
+def test_attention_softmax_temperature_closed_form():
+    # Query 1 sees keys 0 and 1 with q.k = 0 and sqrt(128) ln 3: after the
+    # 1/sqrt(128) scaling the softmax weights are 1/4 and 3/4, so values 4 and
+    # 8 average to 7 (exact in BF16), and P|v| is 7 as well.
+    s = 2
+    q = np.zeros((16, s, 128))
+    k = np.zeros((8, s, 128))
+    v = np.zeros((8, s, 128))
+    q[:, 1, 0] = 1.0
+    k[:, 1, 0] = math.sqrt(128.0) * math.log(3.0)
+    v[:, 0, :], v[:, 1, :] = 4.0, 8.0
+    out, mag = L.attention(q, k, v)
+    out, mag = out.reshape(s, 16, 128), mag.reshape(s, 16, 128)
+    np.testing.assert_allclose(out[1], 7.0, rtol=2.0 ** -8)
+    np.testing.assert_allclose(mag[1], 7.0, rtol=1e-12)
+    assert np.all(out[0] == 4.0)
 
 
 def test_rms_norm_constant_rows_and_swiglu():
