@@ -15,7 +15,8 @@ Prints one JSON line.  `value` is GEMM TFLOP/s of the whole step (the 12 GEMMs'
 2*M*N*K divided by the step time, quantisers included).  `roofline` covers
 the dominant kernel (the block GEMM), timed with HIP events on the stream the
 kernels run on.  `cpu_baseline` times the numpy oracle on a bounded token
-sample of the same layer.
+sample of the same layer with all host threads, and on a smaller sample with
+one thread (`single_thread`).
 """
 
 import argparse
@@ -42,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-single-thread-tokens", type=int, default=256)
     ap.add_argument("--no-fp8-path", action="store_true", help="skip timing the FP8 matrix-core GEMM path")
     ap.add_argument("--no-bf16-baseline", action="store_true", help="skip timing the BF16 GEMMs of the same shapes")
     ap.add_argument("--no-fusion", action="store_true", help="skip timing the fused producers")
@@ -128,34 +130,49 @@ class LayerBuffers:
         rec(3)
 
 
-def cpu_baseline(W, layers, sample_tokens):
-    """The numpy oracle on the first `sample_tokens` tokens of every linear of the layer."""
+def cpu_baseline(W, layers, sample_tokens, single_thread_tokens):
+    """The numpy oracle on the first `sample_tokens` tokens of every linear of the
+    layer with all host threads, then on the first `single_thread_tokens` with
+    one BLAS thread (the oracle itself is the same code either way)."""
     import numpy as np
     from oracle import gemm, quant
+
+    def run(tokens):
+        flops = 0
+        t0 = time.perf_counter()
+        for L in layers:
+            xs, dys = L.xb[:tokens], L.dyb[:tokens]
+            xq, sx = quant.quant_1x128_rows(xs)
+            xqT, sxT = quant.quant_1x128_tokens(xs)
+            wq, sw = quant.quant_128x128(L.wb)
+            wqT, swT = quant.quant_128x128(np.ascontiguousarray(L.wb.T))
+            dyq, sdy = quant.quant_1x128_rows(dys)
+            dyqT, sdyT = quant.quant_1x128_tokens(dys)
+            gemm.fwd(xq, sx, wq, sw, budget=False)
+            gemm.dgrad(dyq, sdy, wqT, swT, budget=False)
+            gemm.wgrad(dyqT, sdyT, xqT, sxT, budget=False)
+            flops += 3 * 2 * tokens * L.n * L.k
+        return flops, time.perf_counter() - t0
+
+    def sample(tokens, dt, threads):
+        return (f"one layer's 4 linears (quantisers + fwd/dgrad/wgrad) on the first {tokens} tokens, "
+                f"numpy float64 oracle, {threads} BLAS thread(s), {dt:.1f} s")
+
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
-    flops = 0
-    t0 = time.perf_counter()
-    for L in layers:
-        xs, dys = L.xb[:sample_tokens], L.dyb[:sample_tokens]
-        xq, sx = quant.quant_1x128_rows(xs)
-        xqT, sxT = quant.quant_1x128_tokens(xs)
-        wq, sw = quant.quant_128x128(L.wb)
-        wqT, swT = quant.quant_128x128(np.ascontiguousarray(L.wb.T))
-        dyq, sdy = quant.quant_1x128_rows(dys)
-        dyqT, sdyT = quant.quant_1x128_tokens(dys)
-        gemm.fwd(xq, sx, wq, sw, budget=False)
-        gemm.dgrad(dyq, sdy, wqT, swT, budget=False)
-        gemm.wgrad(dyqT, sdyT, xqT, sxT, budget=False)
-        flops += 3 * 2 * sample_tokens * L.n * L.k
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"one layer's 4 linears (quantisers + fwd/dgrad/wgrad) on the first {sample_tokens} "
-                      f"tokens, numpy float64 oracle, {dt:.1f} s"}
+    flops, dt = run(sample_tokens)
+    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle", "sample": sample(sample_tokens, dt, threads)}
+    if threadpool_limits is not None and single_thread_tokens > 0:
+        with threadpool_limits(limits=1):
+            flops1, dt1 = run(single_thread_tokens)
+        out["single_thread"] = {"value": round(flops1 / dt1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                                "sample": sample(single_thread_tokens, dt1, 1)}
+    return out
 
 
 def bf16_baseline(torch, B, layers, steps, warmup, fp8_gemm_ms, fp8_step_ms, fp8_mc_gemm_ms):
@@ -582,7 +599,7 @@ def main():
     if not args.no_bf16_baseline:
         out["bf16_baseline"] = bf16_baseline(torch, B, layers, args.steps, args.warmup, gemm_ms, ms_step, f_gemm_ms)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(W, layers, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(W, layers, args.cpu_sample_tokens, args.cpu_single_thread_tokens)
     print(json.dumps(out), flush=True)
 
 
