@@ -210,6 +210,60 @@ struct ScaleStager {
   }
 };
 
+// Epilogue through LDS.  Stored straight from the MFMA result registers, a
+// wave store touches many rows with a few bytes each (the accumulator layout
+// spreads a lane's values down a column).  Instead each wave writes a band of
+// its output tile (BAND rows x WN columns) into a private LDS region, reads it
+// back row-major and stores whole 16-byte chunks: one wave instruction then
+// covers complete WN-column row segments (8 of them for BF16, 4 for FP32).
+// The stage buffers hold the regions once every wave is past the main loop.
+// The row stride is padded by 16 bytes to spread a band's rows over the banks.
+template <int OUT, int WN>
+struct Band {
+  static constexpr int ESZ = OUT == OUT_BF16 ? 2 : 4;
+  static constexpr int RS = WN * ESZ + 16;      // row stride in LDS (bytes)
+  static constexpr int CPR = WN * ESZ / 16;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows per wave instruction
+  static_assert(CPR * RPI == 64, "a band row splits evenly over the wave");
+};
+
+// This wave's region of REGION bytes: regions are packed into the stage
+// buffers (BUF bytes each, NS of them) in wave order.
+template <int REGION, int BUF, int NS, int NW>
+__device__ __forceinline__ uint8_t* band_region(uint8_t* lds0, uint8_t* lds1, uint8_t* lds2, int wave) {
+  constexpr int PER_BUF = BUF / REGION;
+  static_assert(PER_BUF * NS >= NW, "epilogue regions must fit in the stage buffers");
+  const int bi = wave / PER_BUF;
+  return (bi == 0 ? lds0 : bi == 1 ? lds1 : lds2) + (wave % PER_BUF) * REGION;
+}
+
+// Read a band of ROWS rows back from `region` and store row r at output row
+// row0 + r (rows at or past I are skipped), columns col0 .. col0 + WN - 1;
+// OUT_F32_ACC adds the values already in C.
+template <int OUT, int WN, int ROWS>
+__device__ __forceinline__ void store_band(const uint8_t* region, int lane, void* Cout, int64_t ldc,
+                                           int64_t row0, int64_t col0, int64_t I) {
+  using Bd = Band<OUT, WN>;
+  static_assert(ROWS % Bd::RPI == 0, "band rows split over the wave instructions");
+  uint8_t* cbase = static_cast<uint8_t*>(Cout) + col0 * Bd::ESZ;
+#pragma unroll
+  for (int it = 0; it < ROWS / Bd::RPI; ++it) {
+    const int r = it * Bd::RPI + lane / Bd::CPR, k = lane % Bd::CPR;
+    const uint4 w = *reinterpret_cast<const uint4*>(region + r * Bd::RS + k * 16);
+    const int64_t row = row0 + r;
+    if (row >= I) continue;
+    uint8_t* dst = cbase + row * ldc * Bd::ESZ + k * 16;
+    if (OUT == OUT_F32_ACC) {
+      const float4 old = *reinterpret_cast<const float4*>(dst);
+      float4 o = *reinterpret_cast<const float4*>(&w);
+      o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+      *reinterpret_cast<float4*>(dst) = o;
+    } else {
+      *reinterpret_cast<uint4*>(dst) = w;
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int SB_MODE, int PREC, int NW, int NS>
 struct Cfg {
   static constexpr int WGM = BM / WM, WGN = BN / WN;
@@ -399,35 +453,31 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     }
   }
 
-  // Epilogue.  Lane l holds row (l % 32) of each sub-tile and, in
-  // accumulators 4q..4q+3, the four consecutive columns 8q + 4h .. 8q + 4h + 3:
-  // one 8-byte (BF16) or 16-byte (FP32) store each.  The ABI guarantees
-  // 16-byte aligned C with ldc a multiple of 8 (BF16) or 4 (FP32), so these
-  // stores are aligned.
+  // Epilogue, one 32-row band (sub-tile row mt) at a time through LDS.  Lane l
+  // holds row (l % 32) of the band and, in accumulators 4q..4q+3 of sub-tile
+  // nt, the four consecutive columns nt * 32 + 8q + 4h .. + 3.
+  lds_barrier();
+  {
+    using Bd = Band<OUT, WN>;
+    uint8_t* region = band_region<32 * Bd::RS, C::kBufBytes, NS, NW>(lds0, lds1, lds2, wave);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t row = i0 + wm * WM + mt * 32 + rr;
-    if (row >= I) continue;
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = j0 + wn * WN + nt * 32 + 8 * q + 4 * h;
-        const float* v = &acc[mt][nt][4 * q];
-        if (OUT == OUT_BF16) {
-          const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + row * ldc + col) = make_uint2(lo, hi);
-        } else {
-          float4* dst = reinterpret_cast<float4*>(static_cast<float*>(Cout) + row * ldc + col);
-          float4 o = make_float4(v[0], v[1], v[2], v[3]);
-          if (OUT == OUT_F32_ACC) {
-            const float4 old = *dst;
-            o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+        for (int q = 0; q < 4; ++q) {
+          const float* v = &acc[mt][nt][4 * q];
+          uint8_t* p = region + rr * Bd::RS + (nt * 32 + 8 * q + 4 * h) * Bd::ESZ;
+          if (OUT == OUT_BF16) {
+            const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
           }
-          *dst = o;
         }
-      }
+      store_band<OUT, WN, 32>(region, lane, Cout, ldc, i0 + wm * WM + mt * 32, j0 + wn * WN, I);
+    }
   }
 }
 
@@ -555,29 +605,27 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     }
   }
 
-  // Epilogue.
+  // Epilogue, one T-row band (sub-tile row mt) at a time through LDS.  Lane l
+  // holds, in accumulator e of sub-tile nt, band row 4 * (l / T) + e and
+  // column nt * T + l % T.
+  lds_barrier();
   {
-    // Row of accumulator e in sub-tile mt, column of sub-tile nt.
+    using Bd = Band<OUT, WN>;
+    uint8_t* region = band_region<T * Bd::RS, C::kBufBytes, NS, NW>(lds0, lds1, lds2, wave);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int e = 0; e < ACC; ++e) {
-        const int64_t row = i0 + wm * WM + mt * T + 4 * (lane >> 4) + e;
-        if (row >= I) continue;
+      for (int e = 0; e < ACC; ++e)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const int64_t col = j0 + wn * WN + nt * T + (lane & (T - 1));
+          uint8_t* p = region + (4 * (lane / T) + e) * Bd::RS + (nt * T + lane % T) * Bd::ESZ;
           const float v = acc[mt][nt][e];
-          if (OUT == OUT_F32) {
-            static_cast<float*>(Cout)[row * ldc + col] = v;
-          } else if (OUT == OUT_F32_ACC) {
-            float* p = static_cast<float*>(Cout) + row * ldc + col;
-            *p = *p + v;
-          } else {
-            static_cast<uint16_t*>(Cout)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(v);
-          }
+          if (OUT == OUT_BF16)
+            *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(v);
+          else
+            *reinterpret_cast<float*>(p) = v;
         }
-      }
+      store_band<OUT, WN, T>(region, lane, Cout, ldc, i0 + wm * WM + mt * T, j0 + wn * WN, I);
     }
   }
 }
@@ -689,25 +737,29 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void bf16_ge
       if (lb + 2 < nLB) step(lds2, lds0, lb + 2);
     }
   }
+  // Epilogue through LDS, one 32-row band at a time (as in the exact path).
+  lds_barrier();
+  {
+    using Bd = Band<OUT, WN>;
+    uint8_t* region = band_region<32 * Bd::RS, kBuf, NS, NW>(lds0, lds1, lds2, wave);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t row = i0 + wm * WM + mt * 32 + rr;
-    if (row >= I) continue;
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = j0 + wn * WN + nt * 32 + 8 * q + 4 * h;
-        const v16f& v = acc[mt][nt];
-        if (OUT == OUT_BF16) {
-          const uint32_t lo = f32_to_bf16_rne(v[4 * q]) | (f32_to_bf16_rne(v[4 * q + 1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[4 * q + 2]) | (f32_to_bf16_rne(v[4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + row * ldc + col) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(Cout) + row * ldc + col) =
-              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) {
+          const v16f& v = acc[mt][nt];
+          uint8_t* p = region + rr * Bd::RS + (nt * 32 + 8 * q + 4 * h) * Bd::ESZ;
+          if (OUT == OUT_BF16) {
+            const uint32_t lo = f32_to_bf16_rne(v[4 * q]) | (f32_to_bf16_rne(v[4 * q + 1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(v[4 * q + 2]) | (f32_to_bf16_rne(v[4 * q + 3]) << 16);
+            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<float4*>(p) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          }
         }
-      }
+      store_band<OUT, WN, 32>(region, lane, Cout, ldc, i0 + wm * WM + mt * 32, j0 + wn * WN, I);
+    }
   }
 }
 
