@@ -6,6 +6,7 @@
   1048832 codes, 2.15 GB).
 * Dual and token-dimension quantisers over 65536 * 128 + 300 tokens (more
   than 65535 token groups; input 2.15 GB, 44 valid tokens in the last group).
+* The BF16 comparison GEMM with A of 2^20 + 300 rows x 1024 BF16 (2.15 GB).
 
 Inputs repeat a small seeded block with a period along the long dimension;
 each period's scales (GEMM) or values (quantisers) are multiplied by its own
@@ -100,6 +101,27 @@ def test_weight_gradient_contraction_past_2_gib(B):
     cols = sample_index(K, 12, rng, must=(0, K - 1, 128))
     got = host(dw)[np.ix_(rows, cols)]
     want, bnd = gemm.block_gemm(full_codes(dyq0[rows]), sdy[rows], full_codes(xq0[cols]), sx[cols])
+    ok, rep = compare.check_fp32(got, want, bnd)
+    assert ok, rep
+
+
+def test_bf16_gemm_operand_past_2_gib(B):
+    import torch
+    rng = np.random.default_rng(74)
+    M, K, N, P = LONG, 1024, 256, 4096
+    a0 = W.normal_bf16((P, K), 1.0, seed=741)
+    b = W.normal_bf16((N, K), 0.02, seed=742)
+    mult = _period_pow2(M, P, 7)
+    say("large bf16 gemm", M, N, K)
+    a_d = torch.from_numpy(a0.view(np.int16)).cuda().view(torch.bfloat16).repeat(-(-M // P), 1)[:M]
+    a_d.mul_(torch.from_numpy(mult).cuda().to(torch.bfloat16)[:, None])       # powers of two: exact
+    assert a_d.numel() * 2 >= 1 << 31
+    c = B.bf16_gemm_nt(a_d, torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16),
+                       out_dtype=torch.float32)
+    rows = sample_index(M, 48, rng, must=(0, P - 1, (1 << 20) - 1, 1 << 20, M // 2, (M // 128) * 128, M - 1))
+    got = host(c[torch.from_numpy(rows).cuda()])
+    a_rows = W.f32_to_bf16_bits(quant.bf16_bits_to_f32(a0[rows % P]) * mult[rows][:, None])
+    want, bnd = gemm.bf16_gemm(a_rows, b)
     ok, rep = compare.check_fp32(got, want, bnd)
     assert ok, rep
 
