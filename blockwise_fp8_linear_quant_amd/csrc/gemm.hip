@@ -220,6 +220,14 @@ struct ScaleStager {
 // covers complete WN-column row segments (8 of them for BF16, 4 for FP32).
 // The stage buffers hold the regions once every wave is past the main loop.
 // The row stride is padded by 16 bytes to spread a band's rows over the banks.
+// Two binary32 values -> packed BF16, round to nearest even (one
+// v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int OUT, int WN>
 struct Band {
   static constexpr int ESZ = OUT == OUT_BF16 ? 2 : 4;
@@ -471,9 +479,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
           const float* v = &acc[mt][nt][4 * q];
           uint8_t* p = region + rr * Bd::RS + (nt * 32 + 8 * q + 4 * h) * Bd::ESZ;
           if (OUT == OUT_BF16) {
-            const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(p) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
           } else {
             *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
           }
@@ -623,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
           uint8_t* p = region + (4 * (lane / T) + e) * Bd::RS + (nt * T + lane % T) * Bd::ESZ;
           const float v = acc[mt][nt][e];
           if (OUT == OUT_BF16)
-            *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(v);
+            *reinterpret_cast<uint16_t*>(p) = (uint16_t)bf16x2(v, 0.0f);
           else
             *reinterpret_cast<float*>(p) = v;
         }
@@ -753,9 +759,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void bf16_ge
           const v16f& v = acc[mt][nt];
           uint8_t* p = region + rr * Bd::RS + (nt * 32 + 8 * q + 4 * h) * Bd::ESZ;
           if (OUT == OUT_BF16) {
-            const uint32_t lo = f32_to_bf16_rne(v[4 * q]) | (f32_to_bf16_rne(v[4 * q + 1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(v[4 * q + 2]) | (f32_to_bf16_rne(v[4 * q + 3]) << 16);
-            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(p) = make_uint2(bf16x2(v[4 * q], v[4 * q + 1]), bf16x2(v[4 * q + 2], v[4 * q + 3]));
           } else {
             *reinterpret_cast<float4*>(p) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
           }
