@@ -356,8 +356,14 @@ struct SrcPlain {   // a BF16 tensor
   __device__ __forceinline__ uint4 load_full(int64_t r, int64_t c0) const { return load8_full(x + r * ldx + c0); }
 };
 
+// Two binary32 values -> packed BF16, round to nearest even (one
+// v_cvt_pk_bf16_f32 on gfx950).  It equals f32_to_bf16_rne on every binary32
+// input except NaNs (checked exhaustively on gfx950), so the fused
+// producers' BF16 values, and the codes formed from them, are unchanged.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // SwiGLU of the gate and up halves of the gate_up projection: silu(g) * u
