@@ -28,7 +28,7 @@ passes run the producer's backward with PyTorch's kernels from the saved inputs.
 
 The three GEMMs form each 128-wide block product exactly by default; with
 ``fp8_matrix_core=True`` they use the FP8 matrix instructions instead (about
-1.5 times the GEMM rate; the hardware truncates small products inside groups
+1.4 times the GEMM rate; the hardware truncates small products inside groups
 of 8 positions, an error up to about 2^-10 of the block's sum of |a*b|).
 """
 
