@@ -332,9 +332,12 @@ class FastLayer(Layer):
 
     def wgrad(self, accumulate=False, dw0=None):
         B = self.B
+        torch = _torch()
         dyqT, sdyT = B.fp8_quant_1x128(self.dy, transpose_out=True)
         xqT, sxT = B.fp8_quant_1x128(self.x, transpose_out=True)
-        dw = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=self.M, fp8_matrix_core=True)
+        dw = torch.from_numpy(dw0).cuda() if accumulate else None
+        dw = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=self.M, dw=dw, accumulate=accumulate,
+                                    fp8_matrix_core=True)
         odyqT, osdyT = quant.quant_1x128_tokens(self.dyb)
         oxqT, osxT = quant.quant_1x128_tokens(self.xb)
         return host(dw), (lambda rows=None, cols=None: gemm.wgrad(odyqT, osdyT, oxqT, osxT, rows, cols))
@@ -367,6 +370,18 @@ def test_fp8_matrix_core_small_gaussian(B, M, N, K):
     _check_fp32_rtol(got, ref, FP8_PATH_RTOL, "fp8 dgrad")
     got, ref = L.wgrad()
     _check_fp32_rtol(got, ref, FP8_PATH_RTOL, "fp8 wgrad")
+    # BF16 outputs and the accumulating weight gradient (the other epilogue branches)
+    for name, fn in (("fp8 fwd bf16", L.fwd), ("fp8 dgrad bf16", L.dgrad)):
+        got, ref = fn(torch.bfloat16)
+        y, bnd = ref()
+        ok, rep = compare.check_bf16(got, y, bnd, rtol=FP8_PATH_RTOL)
+        assert ok, f"{name}: {rep}"
+    dw0 = np.random.default_rng(5).standard_normal((N, K)).astype(np.float32)
+    got, ref = L.wgrad(accumulate=True, dw0=dw0)
+    y, bnd = ref()
+    # the final FP32 add dW + Y rounds once: 2^-24 |dW| = FP8_PATH_RTOL-scaled 2^-14 |dW| at most
+    ok, rep = compare.check_fp32(got, y + dw0, bnd + np.abs(dw0) * 2.0 ** -14, rtol=FP8_PATH_RTOL)
+    assert ok, f"fp8 wgrad accumulate: {rep}"
 
 
 def test_fp8_matrix_core_config1_exact_tolerance(B):
