@@ -45,3 +45,18 @@ def test_read_traffic_rejects_another_source(tmp_path):
     p.write_text(f"source_sha256: {profiling.source_digest()}\ngemm_hbm_bytes_per_launch: 5\n")
     assert profiling.read_traffic(str(p))["gemm_hbm_bytes_per_launch"] == "5"
     assert profiling.read_traffic(str(tmp_path / "missing.txt")) is None
+
+
+def test_stats_summary_sets_rocprof_beside_the_bench_figure(tmp_path):
+    stats = tmp_path / "s.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"])
+        w.writerow([GEMM, 12, 1200000, 100000, 80.0])
+        w.writerow([COPY, 4, 300000, 75000, 20.0])
+    bench = tmp_path / "b.json"
+    bench.write_text('noise\n{"roofline": {"avg_launch_us": 125.0, "launches_per_step": 12, "achieved": 900.0}}\n')
+    text = profiling.stats_summary(str(stats), "cmd", str(bench))
+    assert "12 calls, average 100.00 us" in text
+    assert "bench.py in the same run: average launch 125.00 us over 12 launches per step" in text
+    assert text.strip().endswith("rocprofv3 average / bench.py average: 0.800")
