@@ -29,8 +29,17 @@ bool device_ok() {
   return ok;
 }
 
-// Workgroups of a quantiser that gives each 128 x 128 tile one workgroup.
-inline int64_t tiles128(int64_t rows, int64_t cols) { return (rows + 127) / 128 * ((cols + 127) / 128); }
+// Largest dimension accepted (far beyond any tensor that fits in memory);
+// checked before any arithmetic on the dimensions.
+constexpr int64_t kMaxDim = (int64_t)1 << 40;
+
+// Whether a one-dimensional grid of ceil(rows / rb) x ceil(cols / cb)
+// workgroups fits (rows, cols >= 0).  Each factor is bounded first, so the
+// product cannot overflow.
+inline bool grid_fits(int64_t rows, int64_t rb, int64_t cols, int64_t cb) {
+  if (rows >= kMaxGrid * rb || cols >= kMaxGrid * cb) return false;
+  return ((rows + rb - 1) / rb) * ((cols + cb - 1) / cb) < kMaxGrid;
+}
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -56,7 +65,7 @@ int check_gemm(int64_t I, int64_t J, int64_t L, const void* A, int64_t lda, cons
   // The kernels address the rows of a tile with 32-bit byte offsets from the
   // tile's first row, and number the tiles in one grid dimension.
   if (lda >= kMaxGemmLd || ldb >= kMaxGemmLd) return FP8BLK_UNSUPPORTED_SHAPE;
-  if ((I + 127) / 128 * (J / 128) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
+  if (!grid_fits(I, 128, J, 128)) return FP8BLK_UNSUPPORTED_SHAPE;
   if (sb_rows && ldsb < J) return FP8BLK_INVALID_ARG;
   if (!al16(A) || !al16(B) || lda % 16 != 0 || ldb % 16 != 0) return FP8BLK_MISALIGNED;
   if (!al16(SA) || ldsa % 4 != 0) return FP8BLK_MISALIGNED;
@@ -73,6 +82,7 @@ int fp8_quant_1x128(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x
                     float* scales, int64_t ld_s, void* stream) {
   if (rows < 0 || cols < 0 || (transpose_out != 0 && transpose_out != 1)) return FP8BLK_INVALID_ARG;
   if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (rows >= kMaxDim || cols >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
   if (x_bf16 == nullptr || q == nullptr || scales == nullptr) return FP8BLK_INVALID_ARG;
   if (ld_x < cols) return FP8BLK_INVALID_ARG;
   if (transpose_out == 0) {
@@ -83,8 +93,8 @@ int fp8_quant_1x128(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x
   }
   // Grids: row blocks x column groups (at most 65535) for the row-wise
   // kernel, one dimension of (token group, 256-feature block) otherwise.
-  if (transpose_out == 0 ? ((cols + 127) / 128 > 65535 || (rows + 31) / 32 >= kMaxGrid)
-                         : (rows + 127) / 128 * ((cols + 255) / 256) >= kMaxGrid)
+  if (transpose_out == 0 ? (cols > (int64_t)65535 * 128 || !grid_fits(rows, 32, 1, 1))
+                         : !grid_fits(rows, 128, cols, 256))
     return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(x_bf16) || ld_x % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al4(scales)) return FP8BLK_MISALIGNED;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
@@ -101,11 +111,12 @@ int fp8_quant_1x128_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t
                          uint8_t* qT, int64_t ld_qT, float* scalesT, int64_t ld_sT, void* stream) {
   if (rows < 0 || cols < 0) return FP8BLK_INVALID_ARG;
   if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (rows >= kMaxDim || cols >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
   if (x_bf16 == nullptr || q == nullptr || scales == nullptr || qT == nullptr || scalesT == nullptr)
     return FP8BLK_INVALID_ARG;
   const int64_t mpad = (rows + 127) / 128 * 128;
   if (ld_x < cols || ld_q < cols || ld_s < rows || ld_qT < mpad || ld_sT < cols) return FP8BLK_INVALID_ARG;
-  if (tiles128(rows, cols) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
+  if (!grid_fits(rows, 128, cols, 128)) return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(x_bf16) || ld_x % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al16(qT) || ld_qT % 16 != 0 ||
       !al4(scales) || !al4(scalesT))
     return FP8BLK_MISALIGNED;
@@ -124,7 +135,7 @@ int check_dual_outputs(int64_t rows, int64_t cols, const uint8_t* q, int64_t ld_
   const int64_t mpad = (rows + 127) / 128 * 128;
   if (ld_q < cols || ld_s < rows || ld_qT < mpad || ld_sT < cols) return FP8BLK_INVALID_ARG;
   if (bf16_out != nullptr && ld_out < cols) return FP8BLK_INVALID_ARG;
-  if (tiles128(rows, cols) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
+  if (!grid_fits(rows, 128, cols, 128)) return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(q) || ld_q % 16 != 0 || !al16(qT) || ld_qT % 16 != 0 || !al4(scales) || !al4(scalesT)) return FP8BLK_MISALIGNED;
   if (bf16_out != nullptr && (!al16(bf16_out) || ld_out % 8 != 0)) return FP8BLK_MISALIGNED;
   return FP8BLK_OK;
@@ -137,6 +148,7 @@ int fp8_swiglu_quant_1x128_dual(const void* gate, int64_t ld_gate, const void* u
                                 void* h_bf16, int64_t ld_h, void* stream) {
   if (rows < 0 || cols < 0) return FP8BLK_INVALID_ARG;
   if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (rows >= kMaxDim || cols >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
   if (gate == nullptr || up == nullptr || ld_gate < cols || ld_up < cols) return FP8BLK_INVALID_ARG;
   const int rc = check_dual_outputs(rows, cols, q, ld_q, scales, ld_s, qT, ld_qT, scalesT, ld_sT, h_bf16, ld_h);
   if (rc != FP8BLK_OK) return rc;
@@ -155,6 +167,7 @@ int fp8_rmsnorm_quant_1x128_dual(const void* x, int64_t ld_x, const void* gamma,
                                  void* y_bf16, int64_t ld_y, void* stream) {
   if (rows < 0 || cols < 0 || !(eps >= 0.0f)) return FP8BLK_INVALID_ARG;
   if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (rows >= kMaxDim || cols >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
   if (x == nullptr || gamma == nullptr || rstd == nullptr || ld_x < cols) return FP8BLK_INVALID_ARG;
   const int rc = check_dual_outputs(rows, cols, q, ld_q, scales, ld_s, qT, ld_qT, scalesT, ld_sT, y_bf16, ld_y);
   if (rc != FP8BLK_OK) return rc;
@@ -172,9 +185,10 @@ int fp8_quant_128x128(const void* w_bf16, int64_t rows, int64_t cols, int64_t ld
   if (rows < 0 || cols < 0) return FP8BLK_INVALID_ARG;
   if ((qT == nullptr) != (scalesT == nullptr)) return FP8BLK_INVALID_ARG;
   if (rows == 0 || cols == 0) return FP8BLK_OK;
+  if (rows >= kMaxDim || cols >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
   if (w_bf16 == nullptr || q == nullptr || scales == nullptr) return FP8BLK_INVALID_ARG;
   if (ld_w < cols || ld_q < cols || (qT != nullptr && ld_qT < rows)) return FP8BLK_INVALID_ARG;
-  if (tiles128(rows, cols) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
+  if (!grid_fits(rows, 128, cols, 128)) return FP8BLK_UNSUPPORTED_SHAPE;
   if (!al16(w_bf16) || ld_w % 8 != 0 || !al16(q) || ld_q % 16 != 0 || !al4(scales)) return FP8BLK_MISALIGNED;
   if (qT != nullptr && (!al16(qT) || ld_qT % 16 != 0 || !al4(scalesT))) return FP8BLK_MISALIGNED;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
@@ -198,6 +212,7 @@ int gemm_impl(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa
   if (c_dtype != FP8BLK_OUT_F32 && c_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
   if (accumulate != 0 && accumulate != 1) return FP8BLK_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP8BLK_INVALID_ARG;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
   const int prec = flags == FP8BLK_GEMM_FP8_MATRIX_CORE ? 1 : 0;
   int64_t I, J, L;
   int sb_mode, out;
@@ -279,8 +294,8 @@ int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,
   if (!al16(c) || ld_c % (out == OUT_BF16 ? 8 : 4) != 0) return FP8BLK_MISALIGNED;
   if (K > 0) {
     if (a == nullptr || b == nullptr || ld_a < K || ld_b < K) return FP8BLK_INVALID_ARG;
-    if (ld_a * 2 >= kMaxGemmLd || ld_b * 2 >= kMaxGemmLd) return FP8BLK_UNSUPPORTED_SHAPE;
-    if ((M + 127) / 128 * (N / 128) >= kMaxGrid) return FP8BLK_UNSUPPORTED_SHAPE;
+    if (ld_a >= kMaxGemmLd / 2 || ld_b >= kMaxGemmLd / 2) return FP8BLK_UNSUPPORTED_SHAPE;
+    if (!grid_fits(M, 128, N, 128)) return FP8BLK_UNSUPPORTED_SHAPE;
     if (!al16(a) || !al16(b) || ld_a % 8 != 0 || ld_b % 8 != 0) return FP8BLK_MISALIGNED;
   }
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;

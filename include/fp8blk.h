@@ -50,7 +50,8 @@
  *     128 x 128 quantisers, (128 tokens x 256 features) blocks for the token
  *     quantiser, 32-row blocks for the row-wise one, whose column count is
  *     also limited to 65535 x 128.  Total operand size is otherwise not
- *     limited (offsets are 64-bit above the tile level).
+ *     limited (offsets are 64-bit above the tile level); any dimension of
+ *     2^40 or more is rejected before arithmetic on it could overflow.
  */
 #ifndef FP8BLK_H
 #define FP8BLK_H

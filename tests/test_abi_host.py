@@ -120,6 +120,13 @@ def test_size_limits_are_per_row_and_per_grid():
     assert lib.fp8_quant_1x128(P, 4, big, big, 0, P, big, P, 4, None) == 2
     assert lib.fp8_quant_1x128_dual(P, big, big, big, P, big, P, big, P, big, P, big, None) == 2
     assert lib.fp8_quant_128x128(P, big, big, big, P, big, P, None, 0, None, None) == 2
+    # absurd sizes are rejected before any arithmetic on them can overflow
+    huge = 1 << 62
+    assert lib.fp8_quant_1x128(P, huge, 128, 128, 1, P, huge, P, 128, None) == 2
+    assert lib.fp8_quant_1x128_dual(P, huge, 128, 128, P, 128, P, huge, P, huge, P, 128, None) == 2
+    assert lib.fp8_block_gemm_wgrad(P, 128, P, 256, P, 128, P, 256, huge, 256, 256, P, 256, 0, None, 0, None) == 2
+    assert lib.fp8_block_gemm_fwd(P, 2048, P, huge, P, 2048, P, huge, 256, 2048, P, 256, 1, None, 0, None) == 2
+    assert lib.bf16_gemm_nt(P, huge, P, 2048, 16, 256, 2048, P, 256, 0, None) == 2
 
 
 def test_binding_raises_without_library(tmp_path):
