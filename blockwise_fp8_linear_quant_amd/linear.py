@@ -206,6 +206,8 @@ class Fp8Linear(torch.nn.Module):
 
 def _rows(x, cols):
     """x as a 2-D [rows, cols] BF16 view with unit column stride and 16-byte aligned rows."""
+    if x.dim() < 1 or x.shape[-1] != cols:
+        raise ValueError(f"input must be [..., {cols}], got {list(x.shape)}")
     x2 = x.reshape(-1, cols)
     if x2.stride(1) != 1 or x2.stride(0) % 8 != 0 or x2.data_ptr() % 16 != 0:
         x2 = x2.contiguous()
