@@ -8,13 +8,15 @@ outputs within the FP32 tolerance or one BF16 ulp -- and nothing outside the
 views may change: every buffer starts filled with a sentinel (0x7F codes,
 NaN scales and outputs) that must survive around the view.  M = 300 gives a
 ragged token tail; K = 384 and N = 256 span several 128-wide blocks and tiles.
+The fused SwiGLU and RMSNorm producers get the same treatment for their
+inputs, their BF16 value output and their four quantised outputs.
 """
 
 import numpy as np
 import pytest
 
 from blockwise_fp8_linear_quant_amd import workloads as W
-from oracle import compare, gemm, quant
+from oracle import compare, fused, gemm, quant
 from tests.gpu_util import host, say
 
 pytestmark = pytest.mark.gpu
@@ -208,3 +210,59 @@ def test_wgrad_on_strided_views(B, operands):
     ok, rep = compare.check_fp32(got, want + dw0, bnd + np.abs(dw0) * 2.0 ** -14)
     assert ok, rep
     assert dw.outside_untouched()
+
+
+def _ulp_diff(a_bits, b_bits):
+    """|a - b| in BF16 ulps (order-preserving integer map of the bit patterns)."""
+    def key(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+def _check_dual_of(h_bits, q, s, qT, sT, label):
+    """The four wide outputs hold the oracle's two 1x128 quantisations of h_bits."""
+    oq, os_ = quant.quant_1x128_rows(h_bits)
+    oqT, osT = quant.quant_1x128_tokens(h_bits)
+    exact(host(q.view), oq, label + " q")
+    exact(host(s.view), os_.T, label + " s")
+    got = host(qT.view)
+    exact(got[:, :M], oqT, label + " qT")
+    assert np.all(got[:, M:] == 0), label + " pads"
+    exact(host(sT.view), osT.T, label + " sT")
+    for w in (q, s, qT, sT):
+        assert w.outside_untouched(), label
+
+
+def _dual_outputs(C):
+    return codes(M, C), f32(C // 128, M), codes(C, MP), f32(MP // 128, C)
+
+
+def test_fused_producers_on_strided_views(B):
+    import torch
+    C = K
+    g = W.normal_bf16((M, C), 1.0, W.seed_for(97, M, C, "x"))
+    u = W.normal_bf16((M, C), 1.0, W.seed_for(97, M, C, "dy"))
+    say("strided swiglu producer", M, C)
+    hw = Wide(M, C, torch.int16, 0x7FC1)
+    q, s, qT, sT = _dual_outputs(C)
+    B.fp8_swiglu_quant_1x128_dual(wide_bf16(g), wide_bf16(u), h_out=hw.view.view(torch.bfloat16),
+                                  q=q.view, scales=s.view, qT=qT.view, scalesT=sT.view)
+    h = host(hw.view).view(np.uint16)
+    assert _ulp_diff(h, fused.swiglu_bf16(g, u)).max() <= 1
+    assert hw.outside_untouched()
+    _check_dual_of(h, q, s, qT, sT, "swiglu")
+
+    x = W.normal_bf16((M, C), 1.0, W.seed_for(97, M, C, "w"))
+    gam = W.f32_to_bf16_bits((np.random.default_rng(97).standard_normal(C) * 0.1 + 1.0).astype(np.float32))
+    gdev = torch.from_numpy(gam.view(np.int16)).cuda().view(torch.bfloat16)
+    say("strided rmsnorm producer", M, C)
+    yw = Wide(M, C, torch.int16, 0x7FC1)
+    q, s, qT, sT = _dual_outputs(C)
+    B.fp8_rmsnorm_quant_1x128_dual(wide_bf16(x), gdev, 1e-6, y_out=yw.view.view(torch.bfloat16),
+                                   q=q.view, scales=s.view, qT=qT.view, scalesT=sT.view)
+    y = host(yw.view).view(np.uint16)
+    want, _ = fused.rmsnorm_bf16(x, gam, 1e-6)
+    assert _ulp_diff(y, want).max() <= 1
+    assert yw.outside_untouched()
+    _check_dual_of(y, q, s, qT, sT, "rmsnorm")
