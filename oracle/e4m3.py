@@ -55,7 +55,8 @@ def encode(values):
     """
     v = np.asarray(values, dtype=np.float32)
     sign = np.signbit(v).astype(np.uint8) << 7
-    a = np.abs(v).astype(np.float64)
+    with np.errstate(invalid="ignore"):      # signalling NaNs raise the invalid flag when widened
+        a = np.abs(v).astype(np.float64)
     nan = np.isnan(a)
     inf = np.isinf(a)
     a = np.where(nan | inf, 0.0, a)
