@@ -549,6 +549,8 @@ def main():
         fast = {"ms_per_step": round(f_ms, 4), "value": round(flops / (f_ms * 1e-3) / 1e12, 3),
                 "gemm_tflops": round(flops / (f_gemm_ms * 1e-3) / 1e12, 3),
                 "gemm_frac_of_fp8_peak": round(flops / (f_gemm_ms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                "gemm_ms_per_step": round(f_gemm_ms, 4), "launches_per_step": n_launch,
+                "avg_launch_us": round(f_gemm_ms / n_launch * 1e3, 2),
                 "note": "fp8_block_gemm with FP8BLK_GEMM_FP8_MATRIX_CORE: v_mfma_f32_16x16x128_f8f6f4 block "
                         "products, hardware-truncated inside groups of 8 (not the default path)"}
 

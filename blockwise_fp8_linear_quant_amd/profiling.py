@@ -36,6 +36,7 @@ import re
 _HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/fp8_codec.h", "build.py")
 GEMM_KERNEL = "block_gemm_f16_kernel"
+FP8_KERNEL = "block_gemm_fp8_kernel"
 COPY_KERNEL_HINTS = ("copy", "elementwise")
 
 
@@ -73,18 +74,20 @@ def stats_summary(stats_csv, command, bench_json=None):
         lines.append(f"{short_name(r['Name'])[:78]:<78} {int(r['Calls']):>6} "
                      f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['TotalDurationNs']) / 1e6:>9.3f} "
                      f"{float(r['Percentage']):>7.2f}")
-    gemm = [r for r in rows if GEMM_KERNEL in r["Name"]]
-    if gemm:
-        calls = sum(int(r["Calls"]) for r in gemm)
-        tot = sum(float(r["TotalDurationNs"]) for r in gemm)
-        avg_us = tot / calls / 1e3
-        lines += ["", f"{GEMM_KERNEL} (all instantiations): {calls} calls, average {avg_us:.2f} us"]
-        if bench_json:
-            # bench.py's own figure from the same profiled process: HIP events
-            # around the timed steps on the stream the GEMMs run on.
-            rec = json.loads(open(bench_json).read().strip().splitlines()[-1])["roofline"]
+    bench = json.loads(open(bench_json).read().strip().splitlines()[-1]) if bench_json else {}
+    # Each GEMM kernel family beside bench.py's own figure from the same
+    # profiled process (HIP events around the timed steps on the GEMMs' stream).
+    for kernel, key, rate in ((GEMM_KERNEL, "roofline", "achieved"), (FP8_KERNEL, "fp8_matrix_core_path", "gemm_tflops")):
+        sel = [r for r in rows if kernel in r["Name"]]
+        if not sel:
+            continue
+        calls = sum(int(r["Calls"]) for r in sel)
+        avg_us = sum(float(r["TotalDurationNs"]) for r in sel) / calls / 1e3
+        lines += ["", f"{kernel} (all instantiations): {calls} calls, average {avg_us:.2f} us"]
+        rec = bench.get(key)
+        if rec and "avg_launch_us" in rec:
             lines += [f"bench.py in the same run: average launch {rec['avg_launch_us']:.2f} us over "
-                      f"{rec['launches_per_step']} launches per step, {rec['achieved']:.1f} TFLOP/s",
+                      f"{rec['launches_per_step']} launches per step, {rec[rate]:.1f} TFLOP/s",
                       f"rocprofv3 average / bench.py average: {avg_us / rec['avg_launch_us']:.3f}"]
     return "\n".join(lines) + "\n"
 

@@ -60,3 +60,19 @@ def test_stats_summary_sets_rocprof_beside_the_bench_figure(tmp_path):
     assert "12 calls, average 100.00 us" in text
     assert "bench.py in the same run: average launch 125.00 us over 12 launches per step" in text
     assert text.strip().endswith("rocprofv3 average / bench.py average: 0.800")
+
+
+def test_stats_summary_covers_the_fp8_matrix_path(tmp_path):
+    stats = tmp_path / "s.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"])
+        w.writerow([GEMM, 12, 1200000, 100000, 50.0])
+        w.writerow(["void fp8blk::block_gemm_fp8_kernel<256, 128>(...)", 12, 840000, 70000, 50.0])
+    bench = tmp_path / "b.json"
+    bench.write_text('{"roofline": {"avg_launch_us": 100.0, "launches_per_step": 12, "achieved": 1000.0}, '
+                     '"fp8_matrix_core_path": {"avg_launch_us": 72.0, "launches_per_step": 12, "gemm_tflops": 1400.0}}\n')
+    text = profiling.stats_summary(str(stats), "cmd", str(bench))
+    assert "block_gemm_fp8_kernel (all instantiations): 12 calls, average 70.00 us" in text
+    assert "average launch 72.00 us over 12 launches per step, 1400.0 TFLOP/s" in text
+    assert text.strip().endswith("rocprofv3 average / bench.py average: 0.972")
