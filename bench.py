@@ -14,9 +14,10 @@ timed region holds only kernel launches of libfp8blk.
 Prints one JSON line.  `value` is GEMM TFLOP/s of the whole step (the 12 GEMMs'
 2*M*N*K divided by the step time, quantisers included).  `roofline` covers
 the dominant kernel (the block GEMM), timed with HIP events on the stream the
-kernels run on.  `cpu_baseline` times the numpy oracle on a bounded token
-sample of the same layer with all host threads, and on a smaller sample with
-one thread (`single_thread`).
+kernels run on; its `frac` is taken against the FP8 dense MFMA peak, the
+metric's own.  `cpu_baseline` times the numpy oracle on a bounded token
+sample of the same layer with all host threads, and on the same sample with
+one thread (`single_thread`), quantisers (GB/s) and GEMMs (TFLOP/s) apart.
 """
 
 import argparse
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    ap.add_argument("--cpu-single-thread-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-single-thread-tokens", type=int, default=4096)
     ap.add_argument("--no-fp8-path", action="store_true", help="skip timing the FP8 matrix-core GEMM path")
     ap.add_argument("--no-bf16-baseline", action="store_true", help="skip timing the BF16 GEMMs of the same shapes")
     ap.add_argument("--no-fusion", action="store_true", help="skip timing the fused producers")
@@ -61,11 +62,8 @@ class LayerBuffers:
     def __init__(self, torch, B, W, name, k, n, M, dev, cfg=2, layer=0, outliers=False):
         import numpy as np
         self.name, self.k, self.n, self.M = name, k, n, M
-        self.xb = W.normal_bf16((M, k), 1.0, W.seed_for(cfg, layer, name, "x"))
-        if outliers:   # configuration 4: round(1% of K) input channels scaled by 32
-            self.xb, _ = W.with_outlier_channels(self.xb, 0.01, 32, W.seed_for(cfg, layer, name, "x").spawn(1)[0])
-        self.wb = W.normal_bf16((n, k), 0.02, W.seed_for(cfg, layer, name, "w"))
-        self.dyb = W.normal_bf16((M, n), 1e-3, W.seed_for(cfg, layer, name, "dy"))
+        # outliers (the 8192-token sweep): round(1% of K) input channels scaled by 32
+        self.xb, self.wb, self.dyb = W.layer_tensors(cfg, layer, name, M, outliers=outliers)
         to = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         self.x, self.w, self.dy = to(self.xb), to(self.wb), to(self.dyb)
         # Outputs (allocated once, reused every step).
@@ -94,9 +92,10 @@ class LayerBuffers:
         wgrad = n * mp + k * mp + 4 * (n + k) * (mp // 128) + 4 * n * k
         return [fwd, dgrad, wgrad]
 
-    def quant_bytes(self, dual=True):
-        """Algorithmic HBM bytes of the step's quantisers (inputs read once per kernel)."""
-        M, n, k = self.M, self.n, self.k
+    def quant_bytes(self, dual=True, M=None):
+        """Algorithmic HBM bytes of the step's quantisers (inputs read once per kernel),
+        at M tokens (default: the buffers' token count)."""
+        M, n, k = (self.M if M is None else M), self.n, self.k
         row = lambda r, c: r * c * 3 + r * (-(-c // 128)) * 4          # 2 B in, 1 B out, scales
         tok = lambda r, c: r * c * 2 + c * (-(-r // 128) * 128) + c * (-(-r // 128)) * 4
         blk = n * k * 2 + 2 * n * k + 2 * 4 * (-(-n // 128)) * (-(-k // 128))
@@ -130,33 +129,60 @@ class LayerBuffers:
         rec(3)
 
 
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(W, layers, sample_tokens, single_thread_tokens):
     """The numpy oracle on the first `sample_tokens` tokens of every linear of the
     layer with all host threads, then on the first `single_thread_tokens` with
-    one BLAS thread (the oracle itself is the same code either way)."""
+    one BLAS thread (the oracle itself is the same code either way).
+
+    Quantisers and GEMMs are timed apart: the GEMMs as TFLOP/s (2*M*N*K), the
+    quantisers as GB/s of the GPU step's algorithmic quantiser bytes at the
+    sample's token count (the oracle reads its inputs once per orientation)."""
     import numpy as np
     from oracle import gemm, quant
 
     def run(tokens):
-        flops = 0
-        t0 = time.perf_counter()
+        flops = qbytes = 0
+        tq = tg = 0.0
         for L in layers:
             xs, dys = L.xb[:tokens], L.dyb[:tokens]
+            t0 = time.perf_counter()
             xq, sx = quant.quant_1x128_rows(xs)
             xqT, sxT = quant.quant_1x128_tokens(xs)
             wq, sw = quant.quant_128x128(L.wb)
             wqT, swT = quant.quant_128x128(np.ascontiguousarray(L.wb.T))
             dyq, sdy = quant.quant_1x128_rows(dys)
             dyqT, sdyT = quant.quant_1x128_tokens(dys)
+            t1 = time.perf_counter()
             gemm.fwd(xq, sx, wq, sw, budget=False)
             gemm.dgrad(dyq, sdy, wqT, swT, budget=False)
             gemm.wgrad(dyqT, sdyT, xqT, sxT, budget=False)
+            t2 = time.perf_counter()
+            tq, tg = tq + (t1 - t0), tg + (t2 - t1)
             flops += 3 * 2 * tokens * L.n * L.k
-        return flops, time.perf_counter() - t0
+            qbytes += L.quant_bytes(True, tokens)
+        return flops, qbytes, tq, tg
 
-    def sample(tokens, dt, threads):
-        return (f"one layer's 4 linears (quantisers + fwd/dgrad/wgrad) on the first {tokens} tokens, "
-                f"numpy float64 oracle, {threads} BLAS thread(s), {dt:.1f} s")
+    def report(tokens, threads):
+        flops, qbytes, tq, tg = run(tokens)
+        dt = tq + tg
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+                "gemm_tflops": round(flops / tg / 1e12, 6),
+                "quantiser_gbps": round(qbytes / tq / 1e9, 3),
+                "seconds": {"quantisers": round(tq, 2), "gemms": round(tg, 2)},
+                "sample": (f"one layer's 4 linears (quantisers + fwd/dgrad/wgrad) on the first {tokens} tokens, "
+                           f"numpy float64 oracle, {threads} BLAS thread(s), {dt:.1f} s")}
 
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -164,14 +190,12 @@ def cpu_baseline(W, layers, sample_tokens, single_thread_tokens):
     except Exception:
         threadpool_limits = None
         threads = os.cpu_count() or 1
-    flops, dt = run(sample_tokens)
-    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-           "kind": "oracle", "sample": sample(sample_tokens, dt, threads)}
+    out = report(sample_tokens, threads)
+    out["kind"] = "oracle"
+    out["cpu_model"] = cpu_model()
     if threadpool_limits is not None and single_thread_tokens > 0:
         with threadpool_limits(limits=1):
-            flops1, dt1 = run(single_thread_tokens)
-        out["single_thread"] = {"value": round(flops1 / dt1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                                "sample": sample(single_thread_tokens, dt1, 1)}
+            out["single_thread"] = report(single_thread_tokens, 1)
     return out
 
 
@@ -265,7 +289,10 @@ def producer_fusion(torch, B, layers, steps, warmup):
 
     SwiGLU: the down projection's input from the gate and up halves of the
     gate_up forward output [M, 12288]; RMSNorm: the qkv input [M, 2048] with a
-    BF16 gain.  Both write the same codes and scales either way.
+    BF16 gain.  The two forms round differently: the fused SwiGLU rounds
+    silu(g) * u once to BF16, PyTorch's F.silu(g) * u rounds silu(g) first and
+    the product again, so a few codes can differ; the timing compares the
+    same amount of work.
     """
     import torch.nn.functional as F
     gu = [L for L in layers if L.name == "gate_up"][0]
@@ -507,7 +534,7 @@ def main():
     gemm_ms = sum(sum(r) for r in per_gemm)
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["f16"]
+    peak = PEAK_TFLOPS["fp8"]        # the metric's own peak: FP8 dense MFMA
     n_launch = 3 * len(layers)
     alg_bytes = sum(sum(L.gemm_bytes()) for L in layers) / n_launch
     gemms = {}
@@ -572,6 +599,7 @@ def main():
                    "tokens": M, "hidden": 2048, "intermediate": 6144, "gemm_gflop_per_step": round(flops / 1e9, 3)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / peak, 4),
+                     "frac_of_issued_f16_peak": round(gemm_tflops / PEAK_TFLOPS["f16"], 4),
                      "traffic": round(traffic) if traffic is not None else None,
                      "algorithmic_bytes_per_launch": round(alg_bytes),
                      "kernel": "block_gemm_f16_kernel (E4M3 codes -> exact F16 MFMA, FP32 block rescale)",
@@ -579,7 +607,8 @@ def main():
                      "avg_launch_us": round(gemm_ms / n_launch * 1e3, 2),
                      "gemm_ms_per_step": round(gemm_ms, 4),
                      "gemm_ms_per_step_p10_p50_p90": [round(v, 4) for v in gemm_spread],
-                     "frac_of_fp8_peak": round(gemm_tflops / PEAK_TFLOPS["fp8"], 4)},
+                     "note": "peak = FP8 dense MFMA (the metric's); the exact path issues F16 matrix "
+                             "instructions, whose dense peak is half of it (frac_of_issued_f16_peak)"},
         "gemms": gemms,
         "quantisers": {"ms_per_step": round(quant_ms, 4), "algorithmic_gb": round(qbytes / 1e9, 4),
                        "gbps": round(qbytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms > 0 else None,

@@ -18,8 +18,13 @@ library's kernels):
   (BF16) and dW += dYqT . XqT (FP32, accumulated into ``weight.main_grad``
   across micro-batches, the FP32 gradient the optimizer reads).
 * the FP8 weight, its transposed copy and their block scales are made once per
-  weight value and reused by every micro-batch until the weight changes (the
-  cache is keyed on the parameter's in-place version counter).
+  weight value and reused by every micro-batch until the weight changes.  The
+  cache is keyed on the parameter's in-place version counter and storage, so
+  in-place updates through the parameter itself (an optimizer's ``p.add_``,
+  ``p.copy_`` under ``no_grad``) rebuild it.  Writes that bypass the counter --
+  through ``weight.data`` or another tensor aliasing the same storage, as a
+  master-to-model weight copy often does -- are not seen: call
+  ``Fp8Linear.invalidate_weight_cache()`` after them.
 
 Two fused entry points put the producer of the linear's input into its
 quantiser: ``forward_rmsnorm`` (RMSNorm, for the qkv and gate_up projections)
@@ -46,6 +51,10 @@ class _WeightCache:
         self.ptr = None
         self.tensors = None
         self.builds = 0
+
+    def invalidate(self):
+        """Force a rebuild on the next use (after writes the version counter misses)."""
+        self.version = self.ptr = None
 
     def get(self, w):
         key = (w._version, w.data_ptr())
@@ -168,6 +177,13 @@ class Fp8Linear(torch.nn.Module):
         self.in_features, self.out_features = in_features, out_features
         self._cache = _WeightCache()
         self.fp8_matrix_core = bool(fp8_matrix_core)
+
+    def invalidate_weight_cache(self):
+        """Requantise the weight on the next forward.  Needed after writes that do
+        not bump the parameter's version counter, e.g. ``weight.data.copy_(w)``
+        or a copy into a tensor that aliases the weight's storage; in-place
+        operations on the parameter itself are detected without it."""
+        self._cache.invalidate()
 
     @property
     def weight_quantisations(self):

@@ -98,6 +98,22 @@ def student_t_stress(shape, seed, tail_tokens=None):
     return f32_to_bf16_bits(x)
 
 
+def layer_tensors(config, layer, linear, M, outliers=False):
+    """(X, W, dY) BF16 bit arrays of one linear of one layer at M tokens.
+
+    X [M, K] ~ N(0, 1), W [N, K] ~ N(0, 0.02), dY [M, N] ~ N(0, 1e-3), each from
+    its own seed.  outliers=True (the 8192-token sweep) scales round(1% of K)
+    input channels of X by 32 (exact in BF16)."""
+    _, k, n = [l for l in LINEARS if l[0] == linear][0]
+    sx = seed_for(config, layer, linear, "x")
+    x = normal_bf16((M, k), 1.0, sx)
+    if outliers:
+        x, _ = with_outlier_channels(x, 0.01, 32, sx.spawn(1)[0])
+    w = normal_bf16((n, k), 0.02, seed_for(config, layer, linear, "w"))
+    dy = normal_bf16((M, n), 1e-3, seed_for(config, layer, linear, "dy"))
+    return x, w, dy
+
+
 def layer_shapes(M):
     """[(name, X shape, W shape, dY shape)] of one decoder layer at M tokens."""
     return [(n, (M, k), (nout, k), (M, nout)) for n, k, nout in LINEARS]

@@ -54,13 +54,21 @@ def check_bf16(gpu_bits, y, bnd, rtol=FP32_RTOL, atol=FP32_ATOL):
 
 
 def check_exact(gpu, ref):
-    """Bit-exact comparison of two arrays of equal dtype.  Returns (ok, n_mismatch)."""
+    """Bit-exact comparison.  Returns (ok, n_mismatch).
+
+    Both arrays must have the same shape and the same dtype; otherwise the
+    result is (False, -1).  Elements are compared as their stored bit patterns
+    (floating-point values through an unsigned integer view of the same
+    width), so +0 and -0 differ, a denormal differs from zero, and NaNs match
+    only when their payloads match -- the quantisers have exactly one correct
+    output, including the sign of a zero scale or code.
+    """
     a = np.asarray(gpu)
     b = np.asarray(ref)
-    if a.shape != b.shape:
+    if a.shape != b.shape or a.dtype != b.dtype:
         return False, -1
-    if a.dtype.kind == "f":
-        a = a.view(np.uint32 if a.dtype.itemsize == 4 else np.uint64)
-        b = b.view(a.dtype)
+    if a.dtype.kind not in "biu":
+        width = np.dtype("u%d" % a.dtype.itemsize)
+        a, b = a.view(width), b.view(width)
     mism = int(np.count_nonzero(a != b))
     return mism == 0, mism

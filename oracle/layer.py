@@ -34,11 +34,11 @@ def bf16_values(bits):
     return quant.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def rms_norm(x, gamma=None):
-    """x * (mean(x^2) + eps)^-1/2 over the last axis, rounded to BF16, then * gamma (BF16)."""
+def rms_norm(x):
+    """x * (mean(x^2) + eps)^-1/2 over the last axis, rounded once to BF16 (unit gain,
+    as the layer's norms are initialised)."""
     r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + EPS)
-    y = _bf(x * r)
-    return y if gamma is None else _bf(y * gamma)
+    return _bf(x * r)
 
 
 def fp8_linear(h, w_bits, budget=False):
@@ -87,9 +87,23 @@ def attention(q, k, v):
 
 
 def swiglu(gu):
-    """gu [s, 12288] BF16 values -> silu(gate) (BF16) * up, BF16."""
+    """gu [s, 12288] BF16 values -> silu(gate) * up rounded once to BF16.
+
+    This is the reading the fused producer follows: the BF16 value handed to
+    the down projection's quantiser is the exact product rounded once (the
+    pages fix no rounding for the activation).  It is the layer's default
+    composition."""
     g, u = gu[:, :INTER], gu[:, INTER:]
-    return _bf(_bf(g / (1.0 + np.exp(-g))) * u)
+    return _bf(g / (1.0 + np.exp(-g)) * u)
+
+
+def swiglu_separate_ops(gu):
+    """gu [s, 12288] BF16 values -> silu(gate) rounded to BF16, times up,
+    rounded to BF16 again: the composition of two separate BF16 operations
+    (a SiLU, then a multiply), as in the layer variant whose producers are
+    not fused.  It differs from swiglu() by at most about one BF16 ulp."""
+    gate, up = gu[:, :INTER], gu[:, INTER:]
+    return _bf(_bf(gate / (1.0 + np.exp(-gate))) * up)
 
 
 def forward(x_bits, w_qkv, w_o, w_gu, w_down):

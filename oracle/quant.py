@@ -110,13 +110,6 @@ def quant_128x128(w_bits):
     return codes, scales
 
 
-def dequantise_groups(codes, scales, group_axis_len=GROUP):
-    """Dequantise row-wise groups: value[r, c] = D(codes[r, c]) * scales[r, c // 128] (float64)."""
-    L = codes.shape[1]
-    s_full = np.repeat(np.asarray(scales, dtype=np.float64), group_axis_len, axis=1)[:, :L]
-    return e4m3.decode(codes) * s_full
-
-
 def expand_block_scales(block_scales, rows):
     """Per-row view of 128x128 block scales: [ceil(R/128), G] -> [R, G]."""
     return np.repeat(np.asarray(block_scales), GROUP, axis=0)[:rows]

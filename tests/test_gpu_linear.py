@@ -87,6 +87,36 @@ def test_fp8_linear_weight_cache_follows_updates(torch_mod):
     assert torch.equal(y2.float(), (2.0 * y0.float()).to(torch.bfloat16).float())
 
 
+def test_fp8_linear_weight_written_through_data(torch_mod):
+    """A write through weight.data bypasses the version counter; after
+    invalidate_weight_cache() the next forward uses the new weight, bit-equal to
+    a fresh module built on it, and a backward reads the new transposed copy."""
+    torch = torch_mod
+    from blockwise_fp8_linear_quant_amd.linear import Fp8Linear
+    M, K, N = 256, 256, 384
+    wa, wb_ = W.normal_bf16((N, K), 0.02, 15), W.normal_bf16((N, K), 0.02, 16)
+    xb = W.normal_bf16((M, K), 1.0, 17)
+    dyb = W.normal_bf16((M, N), 1e-3, 18)
+    x, dy = dev_bf16(xb).contiguous(), dev_bf16(dyb).contiguous()
+    lin = Fp8Linear(K, N, weight=dev_bf16(wa).contiguous())
+    fresh = Fp8Linear(K, N, weight=dev_bf16(wb_).contiguous())
+    say("Fp8Linear weight.data write")
+    with torch.no_grad():
+        lin(x)
+        lin.weight.data.copy_(dev_bf16(wb_))      # the version counter does not move
+        lin.invalidate_weight_cache()
+    xa = x.clone().requires_grad_(True)
+    xf = x.clone().requires_grad_(True)
+    ya, yf = lin(xa), fresh(xf)
+    ya.backward(dy)
+    yf.backward(dy)
+    torch.cuda.synchronize()
+    assert lin.weight_quantisations == 2
+    assert torch.equal(ya, yf)
+    assert torch.equal(xa.grad, xf.grad)
+    assert torch.equal(lin.weight.main_grad, fresh.weight.main_grad)
+
+
 def _rel(a, b):
     a, b = a.double(), b.double()
     return float((a - b).norm() / b.norm())

@@ -180,14 +180,36 @@ def test_layer_tensors_M4096(B, lin):
     check_dual(B, dy, f"{lin} dY")
 
 
-def test_outlier_channels_M8192(B):
-    """Configuration 4: 8192 tokens, 1% of channels scaled by 32."""
-    x = W.normal_bf16((8192, 2048), 1.0, W.seed_for(4, 0, "qkv", "x"))
-    x, cols = W.with_outlier_channels(x, 0.01, 32, W.seed_for(4, 0, "qkv", "x").spawn(1)[0])
-    assert len(cols) == 20
-    check_rows(B, x, "cfg4 X")
-    check_tokens(B, x, "cfg4 X")
-    check_dual(B, x, "cfg4 X")
+def check_both_orientations(B, bits, label):
+    """Row-wise and token-dimension kernels and the single-read dual kernel, all
+    against one oracle evaluation per orientation (large tensors)."""
+    say("quant rows/tokens/dual", label, bits.shape)
+    M = bits.shape[0]
+    oq, os_ = quant.quant_1x128_rows(bits)
+    oqT, osT = quant.quant_1x128_tokens(bits)
+    x = dev_bf16(bits)
+    q, s = (host(t) for t in B.fp8_quant_1x128(x))
+    qt, st = (host(t) for t in B.fp8_quant_1x128(x, transpose_out=True))
+    dq, ds, dqT, dsT = (host(t) for t in B.fp8_quant_1x128_dual(x))
+    for kern, qT_, sT_, q_, s_ in (("separate", qt, st, q, s), ("dual", dqT, dsT, dq, ds)):
+        assert np.all(qT_[:, M:] == 0), f"{label} {kern}: padding bytes not zero"
+        for name, got, ref in (("q", q_, oq), ("s", s_, os_.T), ("qT", qT_[:, :M], oqT), ("sT", sT_, osT.T)):
+            ok, n = compare.check_exact(np.ascontiguousarray(got), np.ascontiguousarray(ref))
+            assert ok, f"{label} {kern}: {name}: {n} entries differ"
+
+
+@pytest.mark.parametrize("layer", [0, 27])
+@pytest.mark.parametrize("lin", [n for n, _, _ in W.LINEARS])
+def test_outlier_layer_tensors_M8192(B, layer, lin):
+    """Configuration 4: every quantised tensor of the first and last layers' four
+    linears at 8192 tokens (X with 1% of channels x32, W, dY), full tensors."""
+    x, w, dy = W.layer_tensors(4, layer, lin, 8192, outliers=True)
+    K = x.shape[1]
+    big = np.abs(quant.bf16_bits_to_f32(x)).max(axis=0) > 16
+    assert big.sum() >= round(0.01 * K)           # the outlier channels are there
+    check_both_orientations(B, x, f"cfg4 L{layer} {lin} X")
+    check_blocks(B, w, f"cfg4 L{layer} {lin} W")
+    check_both_orientations(B, dy, f"cfg4 L{layer} {lin} dY")
 
 
 def test_stress_ragged_M3000(B):

@@ -9,12 +9,16 @@ Closed forms and special cases that a wiring slip would break:
   scores are scaled by 1/sqrt(128): scores 0 and sqrt(128) ln 3 give the
   weights 1/4 and 3/4 exactly;
 * RMSNorm of a constant row is +-1; silu(gate) (up = 1) equals the pinned
-  fused reference, and the layer rounds it to BF16 before multiplying by up;
+  fused reference; the two SwiGLU compositions (the product rounded once, as
+  the fused producer forms it, and silu rounded before the multiply, as two
+  separate BF16 operations do) each equal a 60-digit evaluation rounded to the
+  nearest BF16 at the same points;
 * the whole layer with zero output projections is the identity (residuals),
   and with a zero down projection it is x + o(attention) alone.
 """
 
 import math
+from decimal import Decimal, getcontext
 
 import numpy as np
 
@@ -97,9 +101,44 @@ def test_rms_norm_constant_rows_and_swiglu():
     gu = np.concatenate([L.bf16_values(g), L.bf16_values(one)], axis=1)
     silu = L.swiglu(gu)           # up = 1: silu(gate) rounded once
     assert np.array_equal(silu, L.bf16_values(fused.swiglu_bf16(g, one)))
+    assert np.array_equal(L.swiglu_separate_ops(gu), silu)   # with up = 1 the second rounding is exact
     u = bf16_bits(rng.standard_normal((2, L.INTER)).astype(np.float32))
     gu = np.concatenate([L.bf16_values(g), L.bf16_values(u)], axis=1)
-    assert np.array_equal(L.swiglu(gu), gemm.round_to_bf16(silu * L.bf16_values(u)))
+    assert np.array_equal(L.swiglu_separate_ops(gu), gemm.round_to_bf16(silu * L.bf16_values(u)))
+
+
+def _dec(v):
+    return Decimal(float(v))
+
+
+def _nearest_bf16_value(d):
+    """Exact nearest BF16 value (ties to even) to the Decimal d, as a float."""
+    if d == 0:
+        return 0.0
+    b0 = int((np.asarray([float(d)], dtype=np.float32).view(np.uint32) >> 16)[0])
+    val = lambda b: Decimal(float(np.uint32(b << 16).view(np.float32)))
+    return float(val(min((b0 - 1, b0, b0 + 1), key=lambda b: (abs(val(b) - d), b & 1))))
+
+
+def test_swiglu_compositions_against_high_precision():
+    """Both SwiGLU compositions against a 60-digit evaluation with exact nearest-BF16
+    rounding: swiglu() rounds silu(g) * u once, swiglu_separate_ops() rounds silu(g)
+    first and the product again; on these inputs the two differ somewhere."""
+    getcontext().prec = 60
+    rng = np.random.default_rng(9)
+    n = 48
+    g = L.bf16_values(bf16_bits(rng.standard_normal((1, n)).astype(np.float32) * 3))
+    u = L.bf16_values(bf16_bits(rng.standard_normal((1, n)).astype(np.float32)))
+    inter = L.INTER
+    gu = np.zeros((1, 2 * inter))
+    gu[0, :n], gu[0, inter:inter + n] = g[0], u[0]
+    once, twice = L.swiglu(gu)[0, :n], L.swiglu_separate_ops(gu)[0, :n]
+    for i in range(n):
+        gd, ud = _dec(g[0, i]), _dec(u[0, i])
+        silu = gd / (1 + (-gd).exp())
+        assert once[i] == _nearest_bf16_value(silu * ud), i
+        assert twice[i] == _nearest_bf16_value(_dec(_nearest_bf16_value(silu)) * ud), i
+    assert (once != twice).any()
 
 
 def _weights(rng, zero=()):

@@ -20,8 +20,8 @@ from concurrent.futures import ThreadPoolExecutor
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-E, Q, G, F, L = ("test_oracle_e4m3.py", "test_oracle_quant.py", "test_oracle_gemm.py", "test_oracle_fused.py",
-                 "test_oracle_layer.py")
+E, Q, G, F, L, C = ("test_oracle_e4m3.py", "test_oracle_quant.py", "test_oracle_gemm.py", "test_oracle_fused.py",
+                    "test_oracle_layer.py", "test_oracle_compare.py")
 
 # (module, original text, planted text, pin files that must catch it)
 MUTATIONS = [
@@ -62,6 +62,11 @@ MUTATIONS = [
      "k, v = np.tile(k, (rep, 1, 1)), np.tile(v, (rep, 1, 1))", [L]),                             # GQA heads
     ("layer.py", "g, u = gu[:, :INTER], gu[:, INTER:]", "u, g = gu[:, :INTER], gu[:, INTER:]", [L]),
     ("layer.py", "np.mean(x * x, axis=-1, keepdims=True) + EPS", "np.sum(x * x, axis=-1, keepdims=True) + EPS", [L]),
+    ("layer.py", "return _bf(g / (1.0 + np.exp(-g)) * u)", "return _bf(_bf(g / (1.0 + np.exp(-g))) * u)", [L]),
+    ("layer.py", "return _bf(_bf(gate / (1.0 + np.exp(-gate))) * up)", "return _bf(gate / (1.0 + np.exp(-gate)) * up)",
+     [L]),                                                                                         # SwiGLU roundings
+    ("compare.py", "a, b = a.view(width), b.view(width)", "pass", [C]),                          # value compare
+    ("compare.py", "if a.shape != b.shape or a.dtype != b.dtype:", "if a.shape != b.shape:", [C]),
 ]
 
 
@@ -89,7 +94,7 @@ def _run(module, old, new, files):
 @pytest.fixture(scope="module")
 def results():
     with ThreadPoolExecutor(4) as ex:
-        base = ex.submit(_run, None, None, None, [E, Q, G, F, L])
+        base = ex.submit(_run, None, None, None, [E, Q, G, F, L, C])
         muts = list(ex.map(lambda m: _run(*m), MUTATIONS))
     return base.result(), muts
 
