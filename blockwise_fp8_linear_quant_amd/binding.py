@@ -246,59 +246,108 @@ def _dtype_code(t):
 
 FLAG_EXACT_BLOCKS = 0
 FLAG_FP8_MATRIX_CORE = 1
+FLAG_SPLIT2 = 2
 OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
 
+# Split-K workspaces, one per (device, stream): zero-filled when allocated (the
+# library needs its counters to start at zero and leaves them at zero), grown
+# when a larger problem needs more.  Calls on one stream are ordered, so they
+# can share one; calls on different streams get different ones.
+_workspaces = {}
 
-def fp8_block_gemm(op, a, sa, b, sb, M, N, K, c, accumulate=False, fp8_matrix_core=False):
-    """The generic C entry point (explicit op and matrix path); c is preallocated."""
+
+def _workspace(workspace, op, M, N, K, split2, device, stream):
+    """(pointer, bytes) of the workspace a GEMM call gets: None/False -> none,
+    a uint8 CUDA tensor -> that tensor, True -> the binding's per-stream one."""
+    if workspace is None or workspace is False:
+        return None, 0
+    if isinstance(workspace, torch.Tensor):
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != device:
+            raise ValueError("workspace must be a contiguous uint8 tensor on the operands' device")
+        return workspace.data_ptr(), workspace.numel()
+    lib = _lib.load()
+    need = int((lib.fp8_block_gemm_split2_workspace_size if split2 else lib.fp8_block_gemm_workspace_size)(
+        op, M, N, K))
+    if need == 0:
+        return None, 0
+    key = (device, stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws.data_ptr(), ws.numel()
+
+
+def fp8_block_gemm(op, a, sa, b, sb, M, N, K, c, accumulate=False, fp8_matrix_core=False, workspace=True,
+                   split2=False):
+    """The generic C entry point (explicit op and matrix path); c is preallocated.
+
+    workspace: True (the binding's zero-initialised per-stream workspace),
+    False/None (none) or a caller-owned uint8 tensor.  split2 forces the
+    contraction split in two whenever the workspace allows it."""
     if op not in (OP_FWD, OP_DGRAD, OP_WGRAD):
         raise ValueError("op must be OP_FWD, OP_DGRAD or OP_WGRAD")
     _check_gemm_operands(op, a, sa, b, sb, M, N, K, c)
     ld_sb = sb.stride(0) if op == OP_WGRAD else 0
+    stream = _stream(a)
+    ws, ws_bytes = _workspace(workspace, op, M, N, K, split2, a.device, stream)
+    flags = (FLAG_FP8_MATRIX_CORE if fp8_matrix_core else FLAG_EXACT_BLOCKS) | (FLAG_SPLIT2 if split2 else 0)
     st = _lib.load().fp8_block_gemm(
-        op, FLAG_FP8_MATRIX_CORE if fp8_matrix_core else FLAG_EXACT_BLOCKS,
-        _ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b), b.stride(0), _ptr(sb), ld_sb,
-        M, N, K, _ptr(c), c.stride(0), _dtype_code(c), 1 if accumulate else 0, None, 0, _stream(a))
+        op, flags, _ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b), b.stride(0), _ptr(sb), ld_sb,
+        M, N, K, _ptr(c), c.stride(0), _dtype_code(c), 1 if accumulate else 0, ws, ws_bytes, stream)
     _lib.check(st, "fp8_block_gemm")
     return c
 
 
-def fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None, fp8_matrix_core=False):
-    """Y[M, N] = Xq . Wq^T with 1x128 row scales sx [K/128, M] and block scales sw [N/128, K/128]."""
+def fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None, fp8_matrix_core=False, workspace=True,
+                       split2=False):
+    """Y[M, N] = Xq . Wq^T with 1x128 row scales sx [K/128, M] and block scales sw [N/128, K/128].
+    workspace / split2: as for fp8_block_gemm."""
     _check_2d(xq, torch.uint8, "xq")
     _check_2d(wq, torch.uint8, "wq")
     M, K = xq.shape
     N = wq.shape[0]
     y = _out((M, N), out_dtype, xq.device, y)
     _check_gemm_operands(OP_FWD, xq, sx, wq, sw, M, N, K, y)
-    if fp8_matrix_core:
-        return fp8_block_gemm(OP_FWD, xq, sx, wq, sw, M, N, K, y, fp8_matrix_core=True)
+    if fp8_matrix_core or split2:
+        return fp8_block_gemm(OP_FWD, xq, sx, wq, sw, M, N, K, y, fp8_matrix_core=fp8_matrix_core,
+                              workspace=workspace, split2=split2)
+    stream = _stream(xq)
+    ws, ws_bytes = _workspace(workspace, OP_FWD, M, N, K, False, xq.device, stream)
     st = _lib.load().fp8_block_gemm_fwd(
         _ptr(xq), xq.stride(0), _ptr(sx), sx.stride(0), _ptr(wq), wq.stride(0), _ptr(sw),
-        M, N, K, _ptr(y), y.stride(0), _dtype_code(y), None, 0, _stream(xq))
+        M, N, K, _ptr(y), y.stride(0), _dtype_code(y), ws, ws_bytes, stream)
     _lib.check(st, "fp8_block_gemm_fwd")
     return y
 
 
-def fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, dx=None, fp8_matrix_core=False):
-    """dX[M, K] = dY . W from dYq [M, N] (row scales sdy [N/128, M]) and WqT [K, N] (scales swT [K/128, N/128])."""
+def fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, dx=None, fp8_matrix_core=False,
+                         workspace=True, split2=False):
+    """dX[M, K] = dY . W from dYq [M, N] (row scales sdy [N/128, M]) and WqT [K, N] (scales swT [K/128, N/128]).
+    workspace / split2: as for fp8_block_gemm."""
     _check_2d(dyq, torch.uint8, "dyq")
     _check_2d(wqT, torch.uint8, "wqT")
     M, N = dyq.shape
     K = wqT.shape[0]
     dx = _out((M, K), out_dtype, dyq.device, dx)
     _check_gemm_operands(OP_DGRAD, dyq, sdy, wqT, swT, M, N, K, dx)
-    if fp8_matrix_core:
-        return fp8_block_gemm(OP_DGRAD, dyq, sdy, wqT, swT, M, N, K, dx, fp8_matrix_core=True)
+    if fp8_matrix_core or split2:
+        return fp8_block_gemm(OP_DGRAD, dyq, sdy, wqT, swT, M, N, K, dx, fp8_matrix_core=fp8_matrix_core,
+                              workspace=workspace, split2=split2)
+    stream = _stream(dyq)
+    ws, ws_bytes = _workspace(workspace, OP_DGRAD, M, N, K, False, dyq.device, stream)
     st = _lib.load().fp8_block_gemm_dgrad(
         _ptr(dyq), dyq.stride(0), _ptr(sdy), sdy.stride(0), _ptr(wqT), wqT.stride(0), _ptr(swT),
-        M, N, K, _ptr(dx), dx.stride(0), _dtype_code(dx), None, 0, _stream(dyq))
+        M, N, K, _ptr(dx), dx.stride(0), _dtype_code(dx), ws, ws_bytes, stream)
     _lib.check(st, "fp8_block_gemm_dgrad")
     return dx
 
 
-def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False, fp8_matrix_core=False):
-    """dW[N, K] (+)= dY^T . X from token-dimension codes dyqT [N, M_pad], xqT [K, M_pad]."""
+def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False, fp8_matrix_core=False,
+                         workspace=True, split2=False):
+    """dW[N, K] (+)= dY^T . X from token-dimension codes dyqT [N, M_pad], xqT [K, M_pad].
+    workspace / split2: as for fp8_block_gemm (the o and down projections' weight
+    gradients are split along the tokens when a workspace is given)."""
     _check_2d(dyqT, torch.uint8, "dyqT")
     _check_2d(xqT, torch.uint8, "xqT")
     N = dyqT.shape[0]
@@ -310,11 +359,14 @@ def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False
             raise ValueError("accumulate=True needs an existing dw")
         dw = torch.empty((N, K), dtype=torch.float32, device=dyqT.device)
     _check_gemm_operands(OP_WGRAD, dyqT, sdyT, xqT, sxT, M, N, K, dw)
-    if fp8_matrix_core:
-        return fp8_block_gemm(OP_WGRAD, dyqT, sdyT, xqT, sxT, M, N, K, dw, accumulate, fp8_matrix_core=True)
+    if fp8_matrix_core or split2:
+        return fp8_block_gemm(OP_WGRAD, dyqT, sdyT, xqT, sxT, M, N, K, dw, accumulate,
+                              fp8_matrix_core=fp8_matrix_core, workspace=workspace, split2=split2)
+    stream = _stream(dyqT)
+    ws, ws_bytes = _workspace(workspace, OP_WGRAD, M, N, K, False, dyqT.device, stream)
     st = _lib.load().fp8_block_gemm_wgrad(
         _ptr(dyqT), dyqT.stride(0), _ptr(sdyT), sdyT.stride(0), _ptr(xqT), xqT.stride(0), _ptr(sxT),
-        sxT.stride(0), M, N, K, _ptr(dw), dw.stride(0), 1 if accumulate else 0, None, 0, _stream(dyqT))
+        sxT.stride(0), M, N, K, _ptr(dw), dw.stride(0), 1 if accumulate else 0, ws, ws_bytes, stream)
     _lib.check(st, "fp8_block_gemm_wgrad")
     return dw
 
@@ -349,6 +401,10 @@ def fp8_e4m3_encode(x, q=None):
 
 def fp8_block_gemm_workspace_size(op, M, N, K):
     return int(_lib.load().fp8_block_gemm_workspace_size(op, M, N, K))
+
+
+def fp8_block_gemm_split2_workspace_size(op, M, N, K):
+    return int(_lib.load().fp8_block_gemm_split2_workspace_size(op, M, N, K))
 
 
 def fp8blk_version():

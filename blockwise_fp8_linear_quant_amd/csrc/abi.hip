@@ -203,40 +203,52 @@ namespace {
 
 // Shared body of the GEMM entry points.  Operand naming follows the generic
 // entry point: a/sa is the row-scaled operand, b/sb the second one.
+// The GEMM's output rows, columns and contraction length (I, J, L) for op.
+void gemm_dims(int op, int64_t M, int64_t N, int64_t K, int64_t& I, int64_t& J, int64_t& L) {
+  if (op == FP8BLK_OP_WGRAD) {
+    I = N; J = K; L = (M + 127) / 128 * 128;
+  } else {
+    I = M;
+    J = op == FP8BLK_OP_FWD ? N : K;
+    L = op == FP8BLK_OP_FWD ? K : N;
+  }
+}
+
 int gemm_impl(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
               const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
               int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, int accumulate,
-              hipStream_t st) {
+              void* ws, size_t ws_bytes, hipStream_t st) {
   if (op != FP8BLK_OP_FWD && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return FP8BLK_INVALID_ARG;
-  if (flags != FP8BLK_GEMM_EXACT_BLOCKS && flags != FP8BLK_GEMM_FP8_MATRIX_CORE) return FP8BLK_INVALID_ARG;
+  const int path = flags & ~FP8BLK_GEMM_SPLIT2;
+  if (path != FP8BLK_GEMM_EXACT_BLOCKS && path != FP8BLK_GEMM_FP8_MATRIX_CORE) return FP8BLK_INVALID_ARG;
+  const bool force_split = (flags & FP8BLK_GEMM_SPLIT2) != 0;
   if (c_dtype != FP8BLK_OUT_F32 && c_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
   if (accumulate != 0 && accumulate != 1) return FP8BLK_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP8BLK_INVALID_ARG;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
-  const int prec = flags == FP8BLK_GEMM_FP8_MATRIX_CORE ? 1 : 0;
+  const int prec = path == FP8BLK_GEMM_FP8_MATRIX_CORE ? 1 : 0;
   int64_t I, J, L;
   int sb_mode, out;
+  // wgrad: C = dW [N, K], contraction over M_pad tokens; fwd: C = Y [M, N]
+  // over K; dgrad: C = dX [M, K] over N.
+  gemm_dims(op, M, N, K, I, J, L);
   if (op == FP8BLK_OP_WGRAD) {
-    // C = dW [N, K]: rows I = N, columns J = K, contraction over M_pad tokens.
     if (c_dtype != FP8BLK_OUT_F32) return FP8BLK_INVALID_ARG;
     if (N % 128 != 0) return FP8BLK_UNSUPPORTED_SHAPE;
-    I = N; J = K; L = (M + 127) / 128 * 128;
     sb_mode = SB_ROWS;
     out = accumulate ? OUT_F32_ACC : OUT_F32;
   } else {
     if (accumulate) return FP8BLK_INVALID_ARG;
-    // fwd: C = Y [M, N] over K;  dgrad: C = dX [M, K] over N.
-    I = M;
-    J = op == FP8BLK_OP_FWD ? N : K;
-    L = op == FP8BLK_OP_FWD ? K : N;
     sb_mode = SB_BLOCK;
     out = c_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
   }
   const int rc = check_gemm(I, J, L, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, sb_mode == SB_ROWS, c, ld_c, out, I);
   if (rc == -1) return FP8BLK_OK;
   if (rc != 0) return rc;
+  if (ws != nullptr && !al16(ws)) return FP8BLK_MISALIGNED;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  launch_block_gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, sb_mode, I, J, L, c, ld_c, out, prec, st);
+  const SplitPlan plan = plan_split(I, J, L, ws, ws_bytes, force_split);
+  launch_block_gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, sb_mode, I, J, L, c, ld_c, out, prec, plan, st);
   return finish();
 }
 
@@ -249,9 +261,8 @@ int fp8_block_gemm_fwd(const uint8_t* xq, int64_t ld_xq, const float* sx, int64_
                        int64_t M, int64_t N, int64_t K,
                        void* y, int64_t ld_y, int y_dtype,
                        void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   return gemm_impl(FP8BLK_OP_FWD, FP8BLK_GEMM_EXACT_BLOCKS, xq, ld_xq, sx, ld_sx, wq, ld_wq, sw, 0, M, N, K,
-                   y, ld_y, y_dtype, 0, static_cast<hipStream_t>(stream));
+                   y, ld_y, y_dtype, 0, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int fp8_block_gemm_dgrad(const uint8_t* dyq, int64_t ld_dyq, const float* sdy, int64_t ld_sdy,
@@ -259,9 +270,8 @@ int fp8_block_gemm_dgrad(const uint8_t* dyq, int64_t ld_dyq, const float* sdy, i
                          int64_t M, int64_t N, int64_t K,
                          void* dx, int64_t ld_dx, int dx_dtype,
                          void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   return gemm_impl(FP8BLK_OP_DGRAD, FP8BLK_GEMM_EXACT_BLOCKS, dyq, ld_dyq, sdy, ld_sdy, wqT, ld_wqT, swT, 0,
-                   M, N, K, dx, ld_dx, dx_dtype, 0, static_cast<hipStream_t>(stream));
+                   M, N, K, dx, ld_dx, dx_dtype, 0, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int fp8_block_gemm_wgrad(const uint8_t* dyqT, int64_t ld_dyqT, const float* sdyT, int64_t ld_sdyT,
@@ -269,18 +279,17 @@ int fp8_block_gemm_wgrad(const uint8_t* dyqT, int64_t ld_dyqT, const float* sdyT
                          int64_t M, int64_t N, int64_t K,
                          float* dw, int64_t ld_dw, int accumulate,
                          void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   return gemm_impl(FP8BLK_OP_WGRAD, FP8BLK_GEMM_EXACT_BLOCKS, dyqT, ld_dyqT, sdyT, ld_sdyT, xqT, ld_xqT, sxT,
-                   ld_sxT, M, N, K, dw, ld_dw, FP8BLK_OUT_F32, accumulate, static_cast<hipStream_t>(stream));
+                   ld_sxT, M, N, K, dw, ld_dw, FP8BLK_OUT_F32, accumulate, ws, ws_bytes,
+                   static_cast<hipStream_t>(stream));
 }
 
 int fp8_block_gemm(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
                    const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
                    int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, int accumulate,
                    void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   return gemm_impl(op, flags, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, M, N, K, c, ld_c, c_dtype, accumulate,
-                   static_cast<hipStream_t>(stream));
+                   ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,
@@ -305,8 +314,23 @@ int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,
 }
 
 size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
-  (void)op; (void)M; (void)N; (void)K;
-  return 0;
+  if (op != FP8BLK_OP_FWD && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  int64_t I, J, L;
+  gemm_dims(op, M, N, K, I, J, L);
+  if (J % 128 != 0 || L % 128 != 0 || (op == FP8BLK_OP_WGRAD && I % 128 != 0) || !grid_fits(I, 128, J, 128))
+    return 0;
+  return split_workspace_bytes(I, J, preferred_splits(I, J, L));
+}
+
+size_t fp8_block_gemm_split2_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
+  if (op != FP8BLK_OP_FWD && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  int64_t I, J, L;
+  gemm_dims(op, M, N, K, I, J, L);
+  if (J % 128 != 0 || L % 128 != 0 || (op == FP8BLK_OP_WGRAD && I % 128 != 0) || !grid_fits(I, 128, J, 128))
+    return 0;
+  return split_workspace_bytes(I, J, 2);
 }
 
 int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, void* stream) {

@@ -98,20 +98,53 @@ __device__ __forceinline__ v8h cvt8(uint32_t w0, uint32_t w1) {
 template <int BM>
 constexpr int group_rows() { return BM == 256 ? 4 : 8; }
 
-template <int GM>
-__device__ __forceinline__ void map_tile(int pid, int nblocks, int tilesM, int tilesN, int& tm, int& tn) {
+// With split-K (S > 1) the grid holds S workgroups per tile: the S splits of a
+// tile are consecutive logical units, so they usually share an XCD.  Returns
+// the tile's index in the grouped order and sets its coordinates and this
+// workgroup's split.
+template <int GM, int S>
+__device__ __forceinline__ int map_tile(int pid, int nblocks, int tilesM, int tilesN, int& tm, int& tn, int& split) {
   // Workgroup pid runs on XCD pid % 8; give each XCD a contiguous logical range.
   const int q = nblocks / 8, r = nblocks % 8;
   const int xcd = pid % 8, local = pid / 8;
   const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  split = logical % S;
+  const int tile = logical / S;
   // Grouped order: GM tile-rows at a time, walking down columns.
   const int per_group = GM * tilesN;
-  const int gid = logical / per_group;
+  const int gid = tile / per_group;
   const int first_m = gid * GM;
   const int gm = min(tilesM - first_m, GM);
-  const int in_group = logical - gid * per_group;
+  const int in_group = tile - gid * per_group;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
+  return tile;
+}
+
+// Split-K rendezvous, called by every thread once its split's FP32 partial
+// tile is stored in the workspace.  The workgroup barrier makes every wave's
+// stores happen before thread 0's count on the tile's counter, which is an
+// agent-scope release (other XCDs have their own L2); the workgroup whose count
+// completes the tile performs the matching acquire and returns true: it reads
+// the other splits' partials and stores the tile.  It also puts the counter
+// back to zero, so a workspace whose counters start at zero is left that way by
+// every call.  One release per workgroup and one acquire per tile keep the
+// cache maintenance these imply off the other workgroups' operand reuse; no
+// workgroup ever waits for another, so the scheme needs no co-residency.
+template <int S>
+__device__ __forceinline__ bool split_arrive(unsigned* counter, int t, int* flag) {
+  __syncthreads();
+  if (t == 0) {
+    const unsigned arrived = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = arrived == S - 1;
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
@@ -294,25 +327,32 @@ struct Cfg {
 
 // Exact path: E4M3 -> F16 in registers, v_mfma_f32_32x32x16_f16; one
 // workgroup per output tile.
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS>
+// Split-K (S > 1): workgroup `split` of a tile contracts over scale blocks
+// [nLBtot * split / S, nLBtot * (split + 1) / S); `part` holds S FP32 partial
+// tiles per output tile, `cnt` one arrival counter per output tile.
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS, int S>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_f16_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
-    int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
+    int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN,
+    float* __restrict__ part, unsigned* __restrict__ cnt) {
   using C = Cfg<BM, BN, WM, WN, SB_MODE, PREC_F16, NW, NS>;
   constexpr int MT = C::MT, NT = C::NT;
   // One distinct LDS object per pipeline stage (see the file comment).
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[NS == 3 ? C::kBufBytes : 16];
+  __shared__ int split_flag;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  int tm, tn;
-  map_tile<group_rows<BM>()>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  int tm, tn, split;
+  const int tile = map_tile<group_rows<BM>(), S>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn, split);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
-  const int nLB = (int)(L / BK);
+  const int nLBtot = (int)(L / BK);
+  const int lb0 = nLBtot * split / S;
+  const int nLB = nLBtot * (split + 1) / S - lb0;   // this split's scale blocks
   // Lane l: row (l % 32) of a 32x32 sub-tile; half h = l / 32 holds K bytes
   // [64h, 64h + 64) of the block.  K slice c (0..3) is the 16 bytes at
   // 64h + 16c, one LDS read per fragment row; MFMA k (0, 1) of the slice takes
@@ -338,12 +378,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   stb.init(ldb, j0, j0 + BN - 1, wave, lane);
   ssa.init(i0, I - 1, wave, lane);
   ssb.init(j0, j0 + BN - 1, wave, lane);
-  auto stage_all = [&](int lb, uint8_t* buf) {
-    sta.issue(A + i0 * lda + (int64_t)lb * BK, buf, wave);
-    stb.issue(B + j0 * ldb + (int64_t)lb * BK, buf + BM * BK, wave);
-    ssa.issue(SA + (int64_t)lb * ldsa + i0, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
+  auto stage_all = [&](int lbl, uint8_t* buf) {
+    const int64_t lb = lb0 + lbl;
+    sta.issue(A + i0 * lda + lb * BK, buf, wave);
+    stb.issue(B + j0 * ldb + lb * BK, buf + BM * BK, wave);
+    ssa.issue(SA + lb * ldsa + i0, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
     if (SB_MODE == SB_ROWS)
-      ssb.issue(SB + (int64_t)lb * ldsb + j0, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
+      ssb.issue(SB + lb * ldsb + j0, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
   };
 
   uint4 qa[2][MT], qb[2][NT];   // raw codes of two K slices (software pipeline)
@@ -410,7 +451,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
       for (int q = 0; q < 4; ++q)
         sbr[nt][q] = (SB_MODE == SB_ROWS) ? *reinterpret_cast<const float4*>(lsb + wn * WN + nt * 32 + 8 * q + 4 * h)
                                           : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-    const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLB + lb] : 1.0f;
+    const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLBtot + lb0 + lb] : 1.0f;
     if (NS == 3 && lb + 2 < nLB)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));   // block lb+1 landed, lb+2 may fly
     else
@@ -463,6 +504,47 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     }
   }
 
+  if (S > 1) {
+    // Split-K: store this split's partial tile lane-major (one 1 KB run per
+    // wave instruction); the last split to arrive adds the S partials in split
+    // order -- its own from registers -- and goes on to store the tile.
+    constexpr int kWave = MT * NT * 16 * 64;    // floats per wave and split
+    float* mine = part + ((int64_t)(tile * S + split) * NW + wave) * kWave + lane * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(mine + ((mt * NT + nt) * 4 + q) * 256) =
+              make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
+    if (!split_arrive<S>(cnt + tile, t, &split_flag)) return;
+    const float* first = part + ((int64_t)tile * S * NW + wave) * kWave + lane * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float4 sum;
+#pragma unroll
+          for (int sp = 0; sp < S; ++sp) {
+            float4 v;
+            if (sp == split)
+              v = make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
+            else
+              v = *reinterpret_cast<const float4*>(first + (int64_t)sp * NW * kWave + ((mt * NT + nt) * 4 + q) * 256);
+            if (sp == 0) {
+              sum = v;
+            } else {
+              sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+            }
+          }
+          acc[mt][nt][4 * q] = sum.x; acc[mt][nt][4 * q + 1] = sum.y;
+          acc[mt][nt][4 * q + 2] = sum.z; acc[mt][nt][4 * q + 3] = sum.w;
+        }
+  }
+
   // Epilogue, one 32-row band (sub-tile row mt) at a time through LDS.  Lane l
   // holds row (l % 32) of the band and, in accumulators 4q..4q+3 of sub-tile
   // nt, the four consecutive columns nt * 32 + 8q + 4h .. + 3.
@@ -490,25 +572,29 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
 }
 
 // FP8 matrix-core path: one workgroup per output tile.
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS>
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS, int S>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
-    int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
+    int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN,
+    float* __restrict__ part, unsigned* __restrict__ cnt) {
   using C = Cfg<BM, BN, WM, WN, SB_MODE, PREC_FP8, NW, NS>;
   constexpr int T = C::T, MT = C::MT, NT = C::NT, ACC = C::ACC;
   // One distinct LDS object per pipeline stage (see the file comment).
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[NS == 3 ? C::kBufBytes : 16];
+  __shared__ int split_flag;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  int tm, tn;
-  map_tile<group_rows<BM>()>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  int tm, tn, split;
+  const int tile = map_tile<group_rows<BM>(), S>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn, split);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
-  const int nLB = (int)(L / BK);
+  const int nLBtot = (int)(L / BK);
+  const int lb0 = nLBtot * split / S;
+  const int nLB = nLBtot * (split + 1) / S - lb0;   // this split's scale blocks
   const int64_t last_row = I - 1;
 
   float acc[MT][NT][ACC];
@@ -527,12 +613,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   stb.init(ldb, j0, j0 + BN - 1, wave, lane);
   ssa.init(i0, last_row, wave, lane);
   ssb.init(j0, j0 + BN - 1, wave, lane);
-  auto stage_all = [&](int lb, uint8_t* buf) {
-    sta.issue(A + i0 * lda + (int64_t)lb * BK, buf, wave);
-    stb.issue(B + j0 * ldb + (int64_t)lb * BK, buf + BM * BK, wave);
-    ssa.issue(SA + (int64_t)lb * ldsa + i0, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
+  auto stage_all = [&](int lbl, uint8_t* buf) {
+    const int64_t lb = lb0 + lbl;
+    sta.issue(A + i0 * lda + lb * BK, buf, wave);
+    stb.issue(B + j0 * ldb + lb * BK, buf + BM * BK, wave);
+    ssa.issue(SA + lb * ldsa + i0, reinterpret_cast<float*>(buf + C::kSaOff), wave, lane);
     if (SB_MODE == SB_ROWS)
-      ssb.issue(SB + (int64_t)lb * ldsb + j0, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
+      ssb.issue(SB + lb * ldsb + j0, reinterpret_cast<float*>(buf + C::kSbOff), wave, lane);
   };
 
   {
@@ -546,7 +633,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
       const uint8_t* tb = cur + BM * BK;
       const float* lsa = reinterpret_cast<const float*>(cur + C::kSaOff);
       const float* lsb = reinterpret_cast<const float*>(cur + C::kSbOff);
-      const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLB + lb] : 1.0f;
+      const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLBtot + lb0 + lb] : 1.0f;
 
       {
         // 16x16 sub-tiles.  Lane l: row (l % 16), K bytes [32 (l / 16), +32).
@@ -613,6 +700,42 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     }
   }
 
+  if (S > 1) {
+    // Split-K, as in the exact path: partial tiles stored lane-major, the last
+    // split to arrive adds them in split order.
+    constexpr int kWave = MT * NT * ACC * 64;   // floats per wave and split
+    static_assert(ACC == 4, "one float4 per sub-tile and lane");
+    float* mine = part + ((int64_t)(tile * S + split) * NW + wave) * kWave + lane * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<float4*>(mine + (mt * NT + nt) * 256) =
+            make_float4(acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]);
+    if (!split_arrive<S>(cnt + tile, t, &split_flag)) return;
+    const float* first = part + ((int64_t)tile * S * NW + wave) * kWave + lane * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float4 sum;
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) {
+          float4 v;
+          if (sp == split)
+            v = make_float4(acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]);
+          else
+            v = *reinterpret_cast<const float4*>(first + (int64_t)sp * NW * kWave + (mt * NT + nt) * 256);
+          if (sp == 0) {
+            sum = v;
+          } else {
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+          }
+        }
+        acc[mt][nt][0] = sum.x; acc[mt][nt][1] = sum.y; acc[mt][nt][2] = sum.z; acc[mt][nt][3] = sum.w;
+      }
+  }
+
   // Epilogue, one T-row band (sub-tile row mt) at a time through LDS.  Lane l
   // holds, in accumulator e of sub-tile nt, band row 4 * (l / T) + e and
   // column nt * T + l % T.
@@ -663,8 +786,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void bf16_ge
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  int tm, tn;
-  map_tile<group_rows<BM>()>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  int tm, tn, split;
+  map_tile<group_rows<BM>(), 1>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn, split);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   const int wm = wave / WGN, wn = wave % WGN;
   const int nLB = (int)(L / BK16);
@@ -781,36 +904,40 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void* __restrict__ C, in
 
 constexpr int kCUs = 256;   // MI355X compute units
 
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS>
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS, int S>
 void launch_cfg(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                 const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
-                int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
+                int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, float* part, unsigned* cnt, hipStream_t st) {
   const int tilesM = (int)((I + BM - 1) / BM), tilesN = (int)(J / BN);
-  const int nTiles = tilesM * tilesN;
+  const int nUnits = tilesM * tilesN * S;
   if (PREC == PREC_F16) {
-    hipLaunchKernelGGL((block_gemm_f16_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS>), dim3(nTiles), dim3(64 * NW), 0,
-                       st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+    hipLaunchKernelGGL((block_gemm_f16_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS, S>), dim3(nUnits), dim3(64 * NW),
+                       0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN, part, cnt);
   } else {
-    hipLaunchKernelGGL((block_gemm_fp8_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS>), dim3(nTiles), dim3(64 * NW), 0,
-                       st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+    hipLaunchKernelGGL((block_gemm_fp8_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS, S>), dim3(nUnits), dim3(64 * NW),
+                       0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN, part, cnt);
   }
 }
 
-// Tile choice: 256 x 128 output tiles (8 waves of 64 x 64, triple-buffered
-// LDS, one workgroup per CU) when they fill every CU for a whole number of
-// rounds; otherwise 128 x 128 tiles (4 waves, double-buffered, two
-// workgroups per CU), whose finer granularity keeps every CU busy in a
-// partial last round (e.g. 384 large tiles would leave half the CUs idle
-// for a third of the time).
+// Tile choice: with a split plan, 256 x 128 tiles split in two along the
+// contraction; otherwise 256 x 128 output tiles (8 waves of 64 x 64,
+// triple-buffered LDS, one workgroup per CU) when they fill every CU for a
+// whole number of rounds, else 128 x 128 tiles (4 waves, double-buffered, two
+// workgroups per CU), whose finer granularity keeps every CU busy in a partial
+// last round.
 template <int SB_MODE, int OUT, int PREC>
 void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                  const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
-                 int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, hipStream_t st) {
-  const int64_t big_tiles = ((I + 255) / 256) * (J / 128);
-  if (big_tiles >= kCUs && big_tiles % kCUs == 0)
-    launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
+                 int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, const SplitPlan& plan, hipStream_t st) {
+  if (plan.splits == 2)
+    launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3, 2>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc,
+                                                              plan.part, plan.counters, st);
+  else if (plan.big_tiles)
+    launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3, 1>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc,
+                                                              nullptr, nullptr, st);
   else
-    launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC, 4, 2>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st);
+    launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC, 4, 2, 1>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc,
+                                                              nullptr, nullptr, st);
 }
 
 template <int OUT>
@@ -829,10 +956,53 @@ void launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
 
 }  // namespace
 
+// Workspace layout of a split plan: a fixed 64 KiB region of 4-byte arrival
+// counters (one per output tile, so at most kMaxSplitTiles tiles are split),
+// then S FP32 partial tiles of 256 x 128 per output tile.  The counter region
+// does not depend on the shape, so one workspace can serve problems of
+// different shapes in turn: no problem's partial tiles ever overlap another
+// problem's counters, and every call leaves the counters it used at zero.
+constexpr int64_t kCounterBytes = 64 * 1024;
+constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
+
+size_t split_workspace_bytes(int64_t I, int64_t J, int splits) {
+  if (splits <= 1) return 0;
+  const int64_t tiles = ((I + 255) / 256) * (J / 128);
+  if (tiles > kMaxSplitTiles) return 0;
+  return (size_t)kCounterBytes + (size_t)tiles * splits * 256 * 128 * 4;
+}
+
+// The split a problem uses by default: none.  Splitting the contraction in two
+// (partial tiles in the workspace, added by the second split to finish) was
+// measured on the layer's under-filled shapes -- the o and down weight
+// gradients, 128 and 384 tiles of 256 x 128 -- and was slower than the
+// unsplit kernels there (59 against 50 us and 160 against 128 us at 4096
+// tokens): each split pays the tile prologue and epilogue, the partial tiles'
+// round trip and one L2 write-back, more than the fuller CUs gain.  Splitting
+// stays available on request (FP8BLK_GEMM_SPLIT2).
+int preferred_splits(int64_t I, int64_t J, int64_t L) {
+  (void)I; (void)J; (void)L;
+  return 1;
+}
+
+SplitPlan plan_split(int64_t I, int64_t J, int64_t L, void* ws, size_t ws_bytes, bool force) {
+  SplitPlan p;
+  const int64_t big = ((I + 255) / 256) * (J / 128);
+  p.big_tiles = big >= kCUs && big % kCUs == 0;
+  const int want = force ? (L / 128 >= 2 ? 2 : 1) : preferred_splits(I, J, L);
+  const size_t need = split_workspace_bytes(I, J, 2);
+  if (want == 2 && need > 0 && ws != nullptr && ws_bytes >= need) {
+    p.splits = 2;
+    p.counters = static_cast<unsigned*>(ws);
+    p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
+  }
+  return p;
+}
+
 void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                        const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb, int sb_mode,
                        int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode,
-                       int prec, hipStream_t st) {
+                       int prec, const SplitPlan& plan, hipStream_t st) {
   if (L == 0) {   // empty contraction: the product is zero
     if (out_mode == OUT_F32_ACC) return;
     const int64_t n = I * J;
@@ -845,10 +1015,10 @@ void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t l
   }
 #define FP8BLK_GEMM_CASE(SBM, OM)                                                              \
   if (sb_mode == SBM && out_mode == OM) {                                                      \
-    if (prec == PREC_FP8)                                                                      \
-      launch_prec<SBM, OM, PREC_FP8>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st); \
-    else                                                                                       \
-      launch_prec<SBM, OM, PREC_F16>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, st); \
+    if (prec == PREC_FP8)                                                                            \
+      launch_prec<SBM, OM, PREC_FP8>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, plan, st); \
+    else                                                                                             \
+      launch_prec<SBM, OM, PREC_F16>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, plan, st); \
     return;                                                                                    \
   }
   FP8BLK_GEMM_CASE(SB_BLOCK, OUT_F32)

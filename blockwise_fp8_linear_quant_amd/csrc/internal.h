@@ -31,6 +31,23 @@ enum SbMode { SB_BLOCK = 0, SB_ROWS = 1 };
 // Output modes.
 enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_F32_ACC = 2 };
 
+// How a block GEMM is laid out over the CUs: 256 x 128 tiles or 128 x 128
+// tiles, and, with a workspace, 256 x 128 tiles split in two along the
+// contraction (counters and partial tiles in the workspace).
+struct SplitPlan {
+  bool big_tiles = false;
+  int splits = 1;
+  unsigned* counters = nullptr;
+  float* part = nullptr;
+};
+// Workspace bytes for `splits` splits of an I x J output (0 for one split).
+size_t split_workspace_bytes(int64_t I, int64_t J, int splits);
+// The split count the launch policy picks for I x J x L given room for it.
+int preferred_splits(int64_t I, int64_t J, int64_t L);
+// The plan for a call: split in two when preferred (or forced) and the
+// workspace holds split_workspace_bytes(I, J, 2); otherwise one split.
+SplitPlan plan_split(int64_t I, int64_t J, int64_t L, void* ws, size_t ws_bytes, bool force);
+
 // C[I, J] = sum_lb SA(i, lb) SB(j, lb) sum_{l in lb} A[i, l] B[j, l]
 //   A [I, lda] codes, SA[lb * ldsa + i];
 //   B [J, ldb] codes; SB_BLOCK: SB[(j / 128) * nLB + lb]; SB_ROWS: SB[lb * ldsb + j].
@@ -38,7 +55,7 @@ enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_F32_ACC = 2 };
 void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                        const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb, int sb_mode,
                        int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode,
-                       int prec, hipStream_t st);
+                       int prec, const SplitPlan& plan, hipStream_t st);
 
 // C[I, J] = sum_l A[i, l] B[j, l] over BF16 operands (A [I, lda], B [J, ldb]);
 // J a multiple of 128, L a multiple of 64; out_mode OUT_F32 or OUT_BF16.

@@ -50,6 +50,41 @@ def test_status_strings_and_version():
     assert lib.fp8_block_gemm_workspace_size(0, 4096, 4096, 2048) == 0
 
 
+def test_workspace_sizes():
+    """No shape is split by default (workspace size 0); the forced split needs a fixed
+    64 KiB counter region plus two FP32 partial tiles of 256 x 128 per output tile."""
+    lib = _lib()
+    FWD, DGRAD, WGRAD = 0, 1, 2
+    size, size2 = lib.fp8_block_gemm_workspace_size, lib.fp8_block_gemm_split2_workspace_size
+    tiles = lambda I, J: ((I + 255) // 256) * (J // 128)
+    need = lambda I, J: 65536 + tiles(I, J) * 2 * 256 * 128 * 4
+    for n, k in ((4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144)):
+        for op in (FWD, DGRAD, WGRAD):
+            assert size(op, 4096, n, k) == 0
+        assert size2(FWD, 4096, n, k) == need(4096, n)
+        assert size2(DGRAD, 4096, n, k) == need(4096, k)
+        assert size2(WGRAD, 4096, n, k) == need(n, k)
+    assert size2(WGRAD, 4096, 2048, 2048) == 65536 + 128 * 2 * 256 * 128 * 4    # 128 tiles: 32 MiB + counters
+    assert size2(FWD, 300, 256, 384) == 65536 + 4 * 2 * 256 * 128 * 4           # 2 x 2 tiles
+    # More than 16384 output tiles (the counter region's capacity): never split.
+    assert size2(FWD, 256 * 129, 128 * 128, 384) == 0
+    # Invalid arguments give 0.
+    assert size2(7, 4096, 2048, 2048) == 0 and size2(WGRAD, -1, 2048, 2048) == 0
+    assert size2(WGRAD, 4096, 2000, 2048) == 0 and size2(FWD, 300, 250, 384) == 0
+
+
+def test_misaligned_workspace_rejected_before_launch():
+    lib = _lib()
+    P = ctypes.c_void_p(16)
+    Q = ctypes.c_void_p(24)      # 8-byte aligned only
+    # wgrad 2048 x 2048 over 4096 tokens with a misaligned workspace
+    assert lib.fp8_block_gemm_wgrad(P, 4096, P, 2048, P, 4096, P, 2048, 4096, 2048, 2048, P, 2048, 0,
+                                    Q, 1 << 30, None) == 3
+    # the generic entry point: unknown flag bits are invalid
+    assert lib.fp8_block_gemm(0, 4, P, 2048, P, 256, P, 2048, P, 0, 256, 256, 2048, P, 256, 0, 0,
+                              None, 0, None) == 1
+
+
 def test_validation_happens_before_launch():
     lib = _lib()
     P = ctypes.c_void_p(16)       # aligned dummy address, never dereferenced on the error paths

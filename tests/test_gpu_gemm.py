@@ -407,3 +407,107 @@ def test_fp8_matrix_core_stress_M3000(B):
     say("fp8 path cfg5 wgrad")
     got, ref = L.wgrad()
     _check_fp32_rtol(got, ref, FP8_PATH_RTOL, "fp8 cfg5 wgrad", rng)
+
+
+# ---------------------------------------------------------------------------
+# Split-K: the contraction split in two, each half's FP32 partial tile stored in
+# the workspace and added by the half that finishes second, in split order.
+
+
+def _split_layer(B, M, N, K, seed):
+    xb = W.normal_bf16((M, K), 1.0, W.seed_for(93, seed, 0, "x"))
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(93, seed, 0, "w"))
+    dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(93, seed, 0, "dy"))
+    return Layer(B, xb, wb, dyb)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 256, 384), (1000, 384, 2048), (129, 128, 256)])
+@pytest.mark.parametrize("mc", [False, True])
+def test_split_k_forced_small(B, M, N, K, mc):
+    """Forced split (FP8BLK_GEMM_SPLIT2) on shapes the oracle checks in full: forward
+    (FP32 and BF16), data gradient and weight gradient (overwrite and accumulate)."""
+    torch = _torch()
+    L = _split_layer(B, M, N, K, M)
+    rtol = 2.0 ** -10 + 1e-5 if mc else compare.FP32_RTOL
+    xq, sx = B.fp8_quant_1x128(L.x)
+    wq, sw, wqT, swT = B.fp8_quant_128x128(L.w, with_transpose=True)
+    dyq, sdy, dyqT, sdyT = B.fp8_quant_1x128_dual(L.dy)
+    xqT, sxT = B.fp8_quant_1x128(L.x, transpose_out=True)
+    oxq, osx = quant.quant_1x128_rows(L.xb)
+    owq, osw = quant.quant_128x128(L.wb)
+    odyq, osdy = quant.quant_1x128_rows(L.dyb)
+    owqT, oswT = quant.quant_128x128(np.ascontiguousarray(L.wb.T))
+    odyqT, osdyT = quant.quant_1x128_tokens(L.dyb)
+    oxqT, osxT = quant.quant_1x128_tokens(L.xb)
+    for od, out in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+        say("split-k forced fwd", out, mc, (M, N, K))
+        y = host(B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=od, fp8_matrix_core=mc, split2=True))
+        yr, bnd = gemm.fwd(oxq, osx, owq, osw)
+        ok, rep = (compare.check_fp32(y, yr, bnd, rtol=rtol) if out == "f32"
+                   else compare.check_bf16(y, yr, bnd, rtol=rtol))
+        assert ok, ("fwd", out, rep)
+    say("split-k forced dgrad", mc, (M, N, K))
+    dx = host(B.fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, fp8_matrix_core=mc, split2=True))
+    yr, bnd = gemm.dgrad(odyq, osdy, owqT, oswT)
+    ok, rep = compare.check_bf16(dx, yr, bnd, rtol=rtol)
+    assert ok, ("dgrad", rep)
+    say("split-k forced wgrad", mc, (M, N, K))
+    yr, bnd = gemm.wgrad(odyqT, osdyT, oxqT, osxT)
+    dw = host(B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, fp8_matrix_core=mc, split2=True))
+    ok, rep = compare.check_fp32(dw, yr, bnd, rtol=rtol)
+    assert ok, ("wgrad", rep)
+    dw0 = np.random.default_rng(M + 1).standard_normal((N, K)).astype(np.float32) * 1e-3
+    dw = torch.from_numpy(dw0).cuda()
+    B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, dw=dw, accumulate=True, fp8_matrix_core=mc, split2=True)
+    ok, rep = compare.check_fp32(host(dw), yr + dw0.astype(np.float64),
+                                 bnd + np.abs(dw0) * (2.0 ** -23 / compare.FP32_RTOL), rtol=rtol)
+    assert ok, ("wgrad accumulate", rep)
+
+
+def test_split_k_deterministic_and_counters_left_zero(B):
+    """Two runs of a split GEMM give identical bits, and the caller-owned workspace's
+    counters are zero again after each call."""
+    torch = _torch()
+    M, N, K = 4096, 2048, 2048              # the o projection's weight gradient
+    L = _split_layer(B, M, N, K, 7)
+    dyqT, sdyT = B.fp8_quant_1x128(L.dy, transpose_out=True)
+    xqT, sxT = B.fp8_quant_1x128(L.x, transpose_out=True)
+    need = B.fp8_block_gemm_split2_workspace_size(B.OP_WGRAD, M, N, K)
+    assert need > 0 and B.fp8_block_gemm_workspace_size(B.OP_WGRAD, M, N, K) == 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    tiles = 65536 // 4                      # the fixed counter region
+    say("split-k determinism", (M, N, K))
+    a = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, workspace=ws, split2=True)
+    torch.cuda.synchronize()
+    assert int(ws[:4 * tiles].view(torch.int32).abs().sum()) == 0
+    ws[4 * tiles:].fill_(0x7F)               # stale partials from earlier calls must not matter
+    # A call of another shape in between (the down projection's weight gradient,
+    # 384 tiles) shares the workspace: its partials must not reach any counter.
+    L2 = _split_layer(B, M, 2048, 6144, 8)
+    d_qT, d_sT = B.fp8_quant_1x128(L2.dy, transpose_out=True)
+    x_qT, x_sT = B.fp8_quant_1x128(L2.x, transpose_out=True)
+    ws2 = torch.zeros(B.fp8_block_gemm_split2_workspace_size(B.OP_WGRAD, M, 2048, 6144), dtype=torch.uint8,
+                      device="cuda")
+    ws2[:ws.numel()].copy_(ws)
+    d = B.fp8_block_gemm_wgrad(d_qT, d_sT, x_qT, x_sT, M=M, workspace=ws2, split2=True)
+    a2 = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, workspace=ws2, split2=True)
+    torch.cuda.synchronize()
+    assert int(ws2[:4 * tiles].view(torch.int32).abs().sum()) == 0
+    assert torch.equal(a.view(torch.int32), a2.view(torch.int32))
+    od_qT, od_sT = quant.quant_1x128_tokens(L2.dyb)
+    ox_qT, ox_sT = quant.quant_1x128_tokens(L2.xb)
+    check_sampled(host(d), lambda r=None, cc=None: gemm.wgrad(od_qT, od_sT, ox_qT, ox_sT, r, cc), "f32",
+                  "split wgrad down (shared workspace)", np.random.default_rng(78), k=24)
+    b = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, workspace=ws, split2=True)
+    torch.cuda.synchronize()
+    assert int(ws[:4 * tiles].view(torch.int32).abs().sum()) == 0
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    # Unsplit (the default): a different summation order, the same rule.
+    c = host(B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, workspace=False))
+    odyqT, osdyT = quant.quant_1x128_tokens(L.dyb)
+    oxqT, osxT = quant.quant_1x128_tokens(L.xb)
+    rng = np.random.default_rng(77)
+    check_sampled(host(a), lambda r=None, cc=None: gemm.wgrad(odyqT, osdyT, oxqT, osxT, r, cc), "f32",
+                  "split wgrad o", rng, k=32)
+    check_sampled(c, lambda r=None, cc=None: gemm.wgrad(odyqT, osdyT, oxqT, osxT, r, cc), "f32",
+                  "unsplit wgrad o", rng, k=32)
