@@ -29,6 +29,8 @@ SIGNATURES = {
                                     _vp, _i64, _i32, _vp, _sz, _vp]),
     "fp8_block_gemm": (_i32, [_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
                               _vp, _i64, _i32, _i32, _vp, _sz, _vp]),
+    "fp8_block_gemm_split2_noalloc": (_i32, [_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                                             _i64, _vp, _i64, _i32, _i32, _vp]),
     "bf16_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _i32, _vp]),
     "fp8_block_gemm_workspace_size": (_sz, [_i32, _i64, _i64, _i64]),
     "fp8_block_gemm_split2_workspace_size": (_sz, [_i32, _i64, _i64, _i64]),

@@ -299,6 +299,21 @@ def fp8_block_gemm(op, a, sa, b, sb, M, N, K, c, accumulate=False, fp8_matrix_co
     return c
 
 
+def fp8_block_gemm_split2_noalloc(op, a, sa, b, sb, M, N, K, c, accumulate=False, fp8_matrix_core=False):
+    """fp8_block_gemm split in two along the contraction, with the library's static
+    scratch instead of a workspace (nothing is allocated); c is preallocated."""
+    if op not in (OP_FWD, OP_DGRAD, OP_WGRAD):
+        raise ValueError("op must be OP_FWD, OP_DGRAD or OP_WGRAD")
+    _check_gemm_operands(op, a, sa, b, sb, M, N, K, c)
+    ld_sb = sb.stride(0) if op == OP_WGRAD else 0
+    st = _lib.load().fp8_block_gemm_split2_noalloc(
+        op, FLAG_FP8_MATRIX_CORE if fp8_matrix_core else FLAG_EXACT_BLOCKS,
+        _ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b), b.stride(0), _ptr(sb), ld_sb,
+        M, N, K, _ptr(c), c.stride(0), _dtype_code(c), 1 if accumulate else 0, _stream(a))
+    _lib.check(st, "fp8_block_gemm_split2_noalloc")
+    return c
+
+
 def fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None, fp8_matrix_core=False, workspace=True,
                        split2=False):
     """Y[M, N] = Xq . Wq^T with 1x128 row scales sx [K/128, M] and block scales sw [N/128, K/128].

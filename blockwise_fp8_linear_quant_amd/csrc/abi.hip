@@ -2,6 +2,8 @@
 // The semantics of each call are documented in include/fp8blk.h.
 #include <string.h>
 
+#include <mutex>
+
 #include "fp8blk.h"
 #include "internal.h"
 
@@ -214,42 +216,83 @@ void gemm_dims(int op, int64_t M, int64_t N, int64_t K, int64_t& I, int64_t& J, 
   }
 }
 
-int gemm_impl(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
-              const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
-              int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, int accumulate,
-              void* ws, size_t ws_bytes, hipStream_t st) {
+// Validated description of a GEMM call (see gemm_validate).
+struct GemmCall {
+  int64_t I = 0, J = 0, L = 0;
+  int sb_mode = SB_BLOCK, out = OUT_F32, prec = 0;
+  bool force_split = false;
+};
+
+// Every argument check of the GEMM entry points, before anything is launched.
+// Returns FP8BLK_OK with g filled in, -1 for a valid no-op, or an error status.
+int gemm_validate(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+                  const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
+                  int64_t M, int64_t N, int64_t K, const void* c, int64_t ld_c, int c_dtype, int accumulate,
+                  GemmCall& g) {
   if (op != FP8BLK_OP_FWD && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return FP8BLK_INVALID_ARG;
   const int path = flags & ~FP8BLK_GEMM_SPLIT2;
   if (path != FP8BLK_GEMM_EXACT_BLOCKS && path != FP8BLK_GEMM_FP8_MATRIX_CORE) return FP8BLK_INVALID_ARG;
-  const bool force_split = (flags & FP8BLK_GEMM_SPLIT2) != 0;
+  g.force_split = (flags & FP8BLK_GEMM_SPLIT2) != 0;
   if (c_dtype != FP8BLK_OUT_F32 && c_dtype != FP8BLK_OUT_BF16) return FP8BLK_INVALID_ARG;
   if (accumulate != 0 && accumulate != 1) return FP8BLK_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP8BLK_INVALID_ARG;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8BLK_UNSUPPORTED_SHAPE;
-  const int prec = path == FP8BLK_GEMM_FP8_MATRIX_CORE ? 1 : 0;
-  int64_t I, J, L;
-  int sb_mode, out;
+  g.prec = path == FP8BLK_GEMM_FP8_MATRIX_CORE ? 1 : 0;
   // wgrad: C = dW [N, K], contraction over M_pad tokens; fwd: C = Y [M, N]
   // over K; dgrad: C = dX [M, K] over N.
-  gemm_dims(op, M, N, K, I, J, L);
+  gemm_dims(op, M, N, K, g.I, g.J, g.L);
   if (op == FP8BLK_OP_WGRAD) {
     if (c_dtype != FP8BLK_OUT_F32) return FP8BLK_INVALID_ARG;
     if (N % 128 != 0) return FP8BLK_UNSUPPORTED_SHAPE;
-    sb_mode = SB_ROWS;
-    out = accumulate ? OUT_F32_ACC : OUT_F32;
+    g.sb_mode = SB_ROWS;
+    g.out = accumulate ? OUT_F32_ACC : OUT_F32;
   } else {
     if (accumulate) return FP8BLK_INVALID_ARG;
-    sb_mode = SB_BLOCK;
-    out = c_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
+    g.sb_mode = SB_BLOCK;
+    g.out = c_dtype == FP8BLK_OUT_BF16 ? OUT_BF16 : OUT_F32;
   }
-  const int rc = check_gemm(I, J, L, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, sb_mode == SB_ROWS, c, ld_c, out, I);
+  return check_gemm(g.I, g.J, g.L, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, g.sb_mode == SB_ROWS, c, ld_c, g.out, g.I);
+}
+
+int gemm_impl(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa, int64_t ld_sa,
+              const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
+              int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype, int accumulate,
+              void* ws, size_t ws_bytes, hipStream_t st) {
+  GemmCall g;
+  const int rc = gemm_validate(op, flags, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, M, N, K, c, ld_c, c_dtype,
+                               accumulate, g);
   if (rc == -1) return FP8BLK_OK;
   if (rc != 0) return rc;
   if (ws != nullptr && !al16(ws)) return FP8BLK_MISALIGNED;
   if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
-  const SplitPlan plan = plan_split(I, J, L, ws, ws_bytes, force_split);
-  launch_block_gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, sb_mode, I, J, L, c, ld_c, out, prec, plan, st);
+  const SplitPlan plan = plan_split(g.I, g.J, g.L, ws, ws_bytes, g.force_split);
+  launch_block_gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, g.sb_mode, g.I, g.J, g.L, c, ld_c, g.out, g.prec, plan,
+                    st);
   return finish();
+}
+
+// Scratch of the allocation-free split GEMM: a file-scope device array, one
+// copy per GPU, holding the 64 KiB counter region and the partial tiles of up
+// to 128 output tiles of 256 x 128 (e.g. a 2048 x 2048 weight gradient).  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in): the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current and kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)64 * 1024 + (size_t)128 * 2 * 256 * 128 * 4;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// This device's address of `scratch` (nullptr if the lookup fails).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
 }
 
 }  // namespace
@@ -290,6 +333,32 @@ int fp8_block_gemm(int op, int flags, const uint8_t* a, int64_t ld_a, const floa
                    void* ws, size_t ws_bytes, void* stream) {
   return gemm_impl(op, flags, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, M, N, K, c, ld_c, c_dtype, accumulate,
                    ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int fp8_block_gemm_split2_noalloc(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa,
+                                  int64_t ld_sa, const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
+                                  int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype,
+                                  int accumulate, void* stream) {
+  GemmCall g;
+  const int rc = gemm_validate(op, flags | FP8BLK_GEMM_SPLIT2, a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, M, N, K, c,
+                               ld_c, c_dtype, accumulate, g);
+  if (rc == -1) return FP8BLK_OK;
+  if (rc != 0) return rc;
+  const size_t need = split_workspace_bytes(g.I, g.J, 2);
+  if (need == 0 || need > kScratchBytes) return FP8BLK_WORKSPACE_TOO_SMALL;
+  if (!device_ok()) return FP8BLK_DEVICE_UNSUPPORTED;
+  void* ws = scratch_address();
+  if (ws == nullptr) return FP8BLK_LAUNCH_FAILED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // The counters must start at zero; every call leaves them so, but a call
+  // that never completed may not have: clear the ones this call uses (a fill
+  // kernel, so the call can also be captured into a graph).
+  const int64_t tiles = ((g.I + 255) / 256) * (g.J / 128);
+  launch_clear_u32(static_cast<unsigned*>(ws), tiles, st);
+  const SplitPlan plan = plan_split(g.I, g.J, g.L, ws, kScratchBytes, true);
+  launch_block_gemm(a, ld_a, sa, ld_sa, b, ld_b, sb, ld_sb, g.sb_mode, g.I, g.J, g.L, c, ld_c, g.out, g.prec, plan,
+                    st);
+  return finish();
 }
 
 int bf16_gemm_nt(const void* a, int64_t ld_a, const void* b, int64_t ld_b,

@@ -902,6 +902,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void* __restrict__ C, in
   }
 }
 
+__global__ __launch_bounds__(256) void clear_u32_kernel(unsigned* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 constexpr int kCUs = 256;   // MI355X compute units
 
 template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS, int S>
@@ -1026,6 +1031,12 @@ void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t l
   FP8BLK_GEMM_CASE(SB_ROWS, OUT_F32)
   FP8BLK_GEMM_CASE(SB_ROWS, OUT_F32_ACC)
 #undef FP8BLK_GEMM_CASE
+}
+
+void launch_clear_u32(unsigned* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return;
+  const unsigned blocks = (unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(clear_u32_kernel, dim3(blocks), dim3(256), 0, st, p, n);
 }
 
 void launch_bf16_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,

@@ -57,6 +57,9 @@ void launch_block_gemm(const uint8_t* A, int64_t lda, const float* SA, int64_t l
                        int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, int out_mode,
                        int prec, const SplitPlan& plan, hipStream_t st);
 
+// Zero n 32-bit words at p (a fill kernel: usable inside a captured graph).
+void launch_clear_u32(unsigned* p, int64_t n, hipStream_t st);
+
 // C[I, J] = sum_l A[i, l] B[j, l] over BF16 operands (A [I, lda], B [J, ldb]);
 // J a multiple of 128, L a multiple of 64; out_mode OUT_F32 or OUT_BF16.
 void launch_bf16_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,

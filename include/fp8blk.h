@@ -261,6 +261,27 @@ int fp8_block_gemm(int op, int flags, const uint8_t* a, int64_t ld_a, const floa
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp8_block_gemm with the contraction split in two (FP8BLK_GEMM_SPLIT2) and no
+ * workspace argument: for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The split's counters and partial tiles live in a static device
+ * array of the library, 64 KiB + 32 MiB per GPU, held until the process ends;
+ * the call allocates nothing and clears the counters it uses with a fill
+ * kernel.  Problems needing more than that -- more than 128 output tiles of
+ * 256 x 128 (fp8_block_gemm_split2_workspace_size > 33619968 bytes), e.g. a
+ * weight gradient larger than 2048 x 2048 -- return
+ * FP8BLK_WORKSPACE_TOO_SMALL before anything is launched.  All calls on one
+ * GPU share the array, so calls that overlap in time on one GPU (different
+ * streams or threads) race; calls on one stream are ordered and safe.
+ * Arguments, layouts and results are those of fp8_block_gemm (flags selects
+ * the matrix path; FP8BLK_GEMM_SPLIT2 is implied).
+ */
+int fp8_block_gemm_split2_noalloc(int op, int flags, const uint8_t* a, int64_t ld_a, const float* sa,
+                                  int64_t ld_sa, const uint8_t* b, int64_t ld_b, const float* sb, int64_t ld_sb,
+                                  int64_t M, int64_t N, int64_t K, void* c, int64_t ld_c, int c_dtype,
+                                  int accumulate, void* stream);
+
+/*
  * Plain BF16 GEMM  C[M, N] = A[M, K] . B[N, K]^T  (no quantisation, FP32
  * accumulation), the BF16 baseline against which the FP8 GEMMs are compared:
  * the pages report the FP8 recipe's throughput relative to BF16 training

@@ -73,6 +73,20 @@ def test_workspace_sizes():
     assert size2(WGRAD, 4096, 2000, 2048) == 0 and size2(FWD, 300, 250, 384) == 0
 
 
+def test_noalloc_split_rejects_problems_beyond_its_scratch():
+    """The allocation-free split GEMM holds 128 output tiles of 256 x 128: a 2048 x 6144
+    weight gradient (384 tiles) is refused before anything is launched; argument
+    errors keep their own status."""
+    lib = _lib()
+    P = ctypes.c_void_p(16)
+    f = lib.fp8_block_gemm_split2_noalloc
+    assert f(2, 0, P, 4096, P, 2048, P, 4096, P, 6144, 4096, 2048, 6144, P, 6144, 0, 0, None) == 4
+    assert f(0, 0, P, 2048, P, 8192, P, 2048, P, 0, 8192, 4096, 2048, P, 4096, 1, 0, None) == 4
+    assert f(2, 0, P, 4096, P, 2048, P, 4096, P, 2000, 4096, 2000, 2048, P, 2048, 0, 0, None) == 2
+    assert f(7, 0, P, 4096, P, 2048, P, 4096, P, 2048, 4096, 2048, 2048, P, 2048, 0, 0, None) == 1
+    assert f(2, 0, None, 0, None, 0, None, 0, None, 0, 4096, 0, 2048, None, 0, 0, 0, None) == 0   # empty
+
+
 def test_misaligned_workspace_rejected_before_launch():
     lib = _lib()
     P = ctypes.c_void_p(16)
