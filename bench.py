@@ -12,10 +12,13 @@ dY ~ N(0,1e-3)) already resident in HBM; outputs are preallocated, so the
 timed region holds only kernel launches of libfp8blk.
 
 Prints one JSON line.  `value` is GEMM TFLOP/s of the whole step (the 12 GEMMs'
-2*M*N*K divided by the step time, quantisers included).  `roofline` covers
-the dominant kernel (the block GEMM), timed with HIP events on the stream the
-kernels run on; its `frac` is taken against the FP8 dense MFMA peak, the
-metric's own.  `cpu_baseline` times the numpy oracle on a bounded token
+2*M*N*K divided by the step time, quantisers included), from K steps between
+two HIP events with no event inside a step (each event record costs the stream
+about 5 us).  `roofline` covers the dominant kernel (the block GEMM), timed in a
+second pass of K steps with one event bracket around each linear's three GEMMs
+on the stream the kernels run on; its `frac` is taken against the FP8 dense
+MFMA peak, the metric's own.  Per-GEMM figures come from K back-to-back
+launches of each GEMM.  `cpu_baseline` times the numpy oracle on a bounded token
 sample of the same layer with all host threads, and on the same sample with
 one thread (`single_thread`), quantisers (GB/s) and GEMMs (TFLOP/s) apart.
 """
@@ -51,6 +54,7 @@ def parse():
     ap.add_argument("--no-fusion", action="store_true", help="skip timing the fused producers")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 28-layer M=8192 sweep")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole decoder layer fwd+bwd")
+    ap.add_argument("--no-small-configs", action="store_true", help="skip the kernel-by-kernel timing of configurations 1 and 5")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -116,17 +120,18 @@ class LayerBuffers:
             B.fp8_quant_1x128(self.dy, q=self.dyq, scales=self.sdy)
             B.fp8_quant_1x128(self.dy, transpose_out=True, q=self.dyqT, scales=self.sdyT)
 
-    def gemms(self, B, fp8_mc=False, ev=None):
-        """The three GEMMs; `ev` (4 events) brackets each launch when given."""
-        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
-        rec(0)
-        B.fp8_block_gemm_fwd(self.xq, self.sx, self.wq, self.sw, y=self.y, fp8_matrix_core=fp8_mc)
-        rec(1)
-        B.fp8_block_gemm_dgrad(self.dyq, self.sdy, self.wqT, self.swT, dx=self.dx, fp8_matrix_core=fp8_mc)
-        rec(2)
-        B.fp8_block_gemm_wgrad(self.dyqT, self.sdyT, self.xqT, self.sxT, M=self.M, dw=self.dw,
-                               fp8_matrix_core=fp8_mc)
-        rec(3)
+    def gemm_calls(self, B, fp8_mc=False):
+        """The forward, data-gradient and weight-gradient GEMM launches, as callables."""
+        return [lambda: B.fp8_block_gemm_fwd(self.xq, self.sx, self.wq, self.sw, y=self.y, fp8_matrix_core=fp8_mc),
+                lambda: B.fp8_block_gemm_dgrad(self.dyq, self.sdy, self.wqT, self.swT, dx=self.dx,
+                                               fp8_matrix_core=fp8_mc),
+                lambda: B.fp8_block_gemm_wgrad(self.dyqT, self.sdyT, self.xqT, self.sxT, M=self.M, dw=self.dw,
+                                               fp8_matrix_core=fp8_mc)]
+
+    def gemms(self, B, fp8_mc=False):
+        """The three GEMMs of this linear."""
+        for f in self.gemm_calls(B, fp8_mc):
+            f()
 
 
 def cpu_model():
@@ -220,15 +225,19 @@ def bf16_baseline(torch, B, layers, steps, warmup, fp8_gemm_ms, fp8_step_ms, fp8
     mk = lambda: torch.cuda.Event(enable_timing=True)
 
     def run(fn):
+        """GEMM ms per step, one event bracket around each linear's three GEMMs (as
+        the FP8 step's GEMM time is taken)."""
         for _ in range(warmup):
             for op in ops:
                 fn(*op)
         torch.cuda.synchronize()
-        evs = [[(mk(), mk()) for _ in ops] for _ in range(steps)]
+        groups = [ops[i:i + 3] for i in range(0, len(ops), 3)]
+        evs = [[(mk(), mk()) for _ in groups] for _ in range(steps)]
         for s in range(steps):
-            for (e0, e1), op in zip(evs[s], ops):
+            for (e0, e1), grp in zip(evs[s], groups):
                 e0.record()
-                fn(*op)
+                for op in grp:
+                    fn(*op)
                 e1.record()
         torch.cuda.synchronize()
         return sum(e0.elapsed_time(e1) for row in evs for e0, e1 in row) / steps
@@ -462,6 +471,89 @@ def quantisers_cold(torch, B, layers, steps, warmup, qbytes, copies=3):
             "input_copies": copies, "input_footprint_gb": round(footprint / 1e9, 2)}
 
 
+def small_configs(torch, B, W, dev, reps=20):
+    """Configurations 1 and 5, kernel by kernel.
+
+    1: X [256, 2048] ~ N(0,1), W [2048, 2048] ~ N(0,0.02): row-wise 1x128
+       quantiser for X, 128x128 for W, forward GEMM with FP32 output.
+    5: the ragged stress case, down projection at 3000 tokens: X [3000, 6144]
+       Student-t with zero groups and spikes, W [2048, 6144], dY [3000, 2048]:
+       dual quantiser for X, 128x128 for W, token-dimension quantiser for dY,
+       forward GEMM (BF16 out) and weight gradient (FP32 out).
+    These launches are shorter than Python takes to issue them, so each rep first
+    queues a spin kernel (torch.cuda._sleep) that keeps the GPU busy while the
+    rep's launches and their events are enqueued; every event pair then brackets
+    one kernel.  Medians over the reps.
+    """
+    import numpy as np
+    to = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    out = {}
+
+    def run(name, kernels, flops, qbytes):
+        for fn, _ in kernels:          # warm-up (and allocation of every output)
+            fn()
+        torch.cuda.synchronize()
+        times = [[] for _ in kernels]
+        s0, s1 = mk(), mk()
+        for _ in range(reps):
+            evs = [(mk(), mk()) for _ in kernels]
+            s0.record()
+            torch.cuda._sleep(2_000_000)
+            s1.record()
+            for (fn, _), (a, b) in zip(kernels, evs):
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            for t, (a, b) in zip(times, evs):
+                t.append(a.elapsed_time(b) * 1e3)
+        med = [float(np.median(t)) for t in times]
+        per = {label: round(us, 2) for (_, label), us in zip(kernels, med)}
+        nq = len(qbytes)
+        q_us, g_us = sum(med[:nq]), sum(med[nq:])
+        out[name] = {"kernel_us": per, "total_us": round(sum(med), 2),
+                     "gemm_tflops": round(flops / (g_us * 1e-6) / 1e12, 1),
+                     "quantiser_gbps": round(sum(qbytes) / (q_us * 1e-6) / 1e9, 1),
+                     "spin_ms": round(s0.elapsed_time(s1), 3)}
+
+    # Configuration 1.
+    x = to(W.normal_bf16((256, 2048), 1.0, W.seed_for(1, 0, "o", "x")))
+    w = to(W.normal_bf16((2048, 2048), 0.02, W.seed_for(1, 0, "o", "w")))
+    xq, sx = B.fp8_quant_1x128(x)
+    wq, sw, _, _ = B.fp8_quant_128x128(w)
+    y = torch.empty((256, 2048), dtype=torch.float32, device=dev)
+    run("config1", [(lambda: B.fp8_quant_1x128(x, q=xq, scales=sx), "quant_1x128 X [256, 2048]"),
+                    (lambda: B.fp8_quant_128x128(w, False, wq, sw), "quant_128x128 W [2048, 2048]"),
+                    (lambda: B.fp8_block_gemm_fwd(xq, sx, wq, sw, y=y), "fwd 256x2048x2048 FP32")],
+        2 * 256 * 2048 * 2048, [256 * 2048 * 3 + 256 * 16 * 4, 2048 * 2048 * 3 + 256 * 4])
+
+    # Configuration 5.
+    M, K, N = 3000, 6144, 2048
+    Mp = -(-M // 128) * 128
+    x = to(W.student_t_stress((M, K), W.seed_for(5, 0, "down", "x")))
+    w = to(W.normal_bf16((N, K), 0.02, W.seed_for(5, 0, "down", "w")))
+    dy = to(W.normal_bf16((M, N), 1e-3, W.seed_for(5, 0, "down", "dy")))
+    xq, sx, xqT, sxT = B.fp8_quant_1x128_dual(x)
+    wq, sw, _, _ = B.fp8_quant_128x128(w)
+    dyqT, sdyT = B.fp8_quant_1x128(dy, transpose_out=True)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    run("config5", [(lambda: B.fp8_quant_1x128_dual(x, xq, sx, xqT, sxT), "dual 1x128 X [3000, 6144]"),
+                    (lambda: B.fp8_quant_128x128(w, False, wq, sw), "quant_128x128 W [2048, 6144]"),
+                    (lambda: B.fp8_quant_1x128(dy, transpose_out=True, q=dyqT, scales=sdyT),
+                     "token-dim 1x128 dY [3000, 2048]"),
+                    (lambda: B.fp8_block_gemm_fwd(xq, sx, wq, sw, y=y), "fwd 3000x2048x6144 BF16"),
+                    (lambda: B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, dw=dw), "wgrad 2048x6144 over 3000")],
+        2 * 2 * M * N * K,
+        [M * K * 2 + M * K + K * Mp + 4 * (M * (K // 128) + K * (Mp // 128)),
+         N * K * 3 + 4 * (N // 128) * (K // 128),
+         M * N * 2 + N * Mp + 4 * N * (Mp // 128)])
+    out["note"] = ("each kernel bracketed by its own events behind a queued spin kernel; quantiser_gbps uses "
+                   "algorithmic bytes (BF16 read once, codes and scales written once)")
+    return out
+
+
 def copy_probe(torch, dev, mib):
     """A plain device copy of known size (float32 multiply by one), launched once.
 
@@ -493,45 +585,75 @@ def main():
     if args.copy_probe_mib:
         copy_probe(torch, dev, args.copy_probe_mib)
 
-    def step(evs=None, fp8_mc=False):
+    def step(fp8_mc=False, marks=None):
+        """One pass over the four linears.  marks[i] (three events) brackets linear
+        i's quantisers and then its three GEMMs when given."""
         for i, L in enumerate(layers):
-            if evs is not None:
-                evs[i][0].record()
+            if marks is not None:
+                marks[i][0].record()
             L.quantise(B, dual=True)
-            L.gemms(B, fp8_mc, evs[i][1:] if evs is not None else None)
+            if marks is not None:
+                marks[i][1].record()
+            L.gemms(B, fp8_mc)
+            if marks is not None:
+                marks[i][2].record()
 
     def timed(fp8_mc):
-        """K timed steps -> (ms/step, per-GEMM ms [linear][op], quantiser ms/step, wall s,
-        p10/p50/p90 over the steps of the 12 GEMM launches' summed time)."""
-        for _ in range(args.warmup):
-            step(fp8_mc=fp8_mc)
-        torch.cuda.synchronize()
+        """Three timed passes of K steps each (after W warm-up steps):
+        1. ms per step, from two events around the K steps only (no event inside a
+           step: each event record costs the stream about 5 us);
+        2. GEMM and quantiser ms per step, from one event bracket around each
+           linear's quantisers and one around its three GEMMs, with the p10/p50/p90
+           of the GEMM time over the steps;
+        3. ms of each GEMM [linear][op], from K launches of it back to back
+           between two events.
+        Returns (ms/step, GEMM ms/step, per-GEMM ms, quantiser ms/step, wall s of
+        pass 1, GEMM spread)."""
         mk = lambda: torch.cuda.Event(enable_timing=True)
-        evs = [[[mk() for _ in range(5)] for _ in layers] for _ in range(args.steps)]
-        start, end = mk(), mk()
+        for _ in range(args.warmup):
+            step(fp8_mc)
         torch.cuda.synchronize()
+        start, end = mk(), mk()
         t_wall = time.perf_counter()
         start.record()
-        for s in range(args.steps):
-            step(evs[s], fp8_mc)
+        for _ in range(args.steps):
+            step(fp8_mc)
         end.record()
         torch.cuda.synchronize()
         t_wall = time.perf_counter() - t_wall
         ms_step = start.elapsed_time(end) / args.steps
-        per_gemm = [[sum(evs[s][i][o + 1].elapsed_time(evs[s][i][o + 2]) for s in range(args.steps)) / args.steps
-                     for o in range(3)] for i in range(len(layers))]
-        quant_ms = sum(evs[s][i][0].elapsed_time(evs[s][i][1])
+
+        marks = [[[mk() for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+        for s in range(args.steps):
+            step(fp8_mc, marks[s])
+        torch.cuda.synchronize()
+        gemm_steps = sorted(sum(marks[s][i][1].elapsed_time(marks[s][i][2]) for i in range(len(layers)))
+                            for s in range(args.steps))
+        gemm_ms = sum(gemm_steps) / args.steps
+        quant_ms = sum(marks[s][i][0].elapsed_time(marks[s][i][1])
                        for s in range(args.steps) for i in range(len(layers))) / args.steps
-        # Per-step sum of the 12 GEMM launches, for the spread across steps.
-        gemm_steps = sorted(sum(evs[s][i][o + 1].elapsed_time(evs[s][i][o + 2])
-                                for i in range(len(layers)) for o in range(3)) for s in range(args.steps))
         pct = lambda q: gemm_steps[min(len(gemm_steps) - 1, int(q * (len(gemm_steps) - 1) + 0.5))]
-        return ms_step, per_gemm, quant_ms, t_wall, [pct(0.1), pct(0.5), pct(0.9)]
+
+        per_gemm = []
+        for L in layers:
+            row = []
+            for f in L.gemm_calls(B, fp8_mc):
+                f()
+                torch.cuda.synchronize()
+                e0, e1 = mk(), mk()
+                e0.record()
+                for _ in range(args.steps):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                row.append(e0.elapsed_time(e1) / args.steps)
+            per_gemm.append(row)
+        return ms_step, gemm_ms, per_gemm, quant_ms, t_wall, [pct(0.1), pct(0.5), pct(0.9)]
 
     # Timed region (default path: exact block products on the F16 matrix path).
-    ms_step, per_gemm, quant_ms, t_wall, gemm_spread = timed(False)
+    ms_step, gemm_ms, per_gemm, quant_ms, t_wall, gemm_spread = timed(False)
     flops = sum(L.flops() for L in layers)
-    gemm_ms = sum(sum(r) for r in per_gemm)
+    gemm_b2b_ms = sum(sum(r) for r in per_gemm)
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["fp8"]        # the metric's own peak: FP8 dense MFMA
@@ -571,14 +693,13 @@ def main():
     fast = None
     f_gemm_ms = None
     if not args.no_fp8_path:
-        f_ms, f_gemm, f_q, _, _ = timed(True)
-        f_gemm_ms = sum(sum(r) for r in f_gemm)
+        f_ms, f_gemm_ms, _, _, _, _ = timed(True)
         fast = {"ms_per_step": round(f_ms, 4), "value": round(flops / (f_ms * 1e-3) / 1e12, 3),
                 "gemm_tflops": round(flops / (f_gemm_ms * 1e-3) / 1e12, 3),
                 "gemm_frac_of_fp8_peak": round(flops / (f_gemm_ms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                 "gemm_ms_per_step": round(f_gemm_ms, 4), "launches_per_step": n_launch,
                 "avg_launch_us": round(f_gemm_ms / n_launch * 1e3, 2),
-                "note": "fp8_block_gemm with FP8BLK_GEMM_FP8_MATRIX_CORE: v_mfma_f32_16x16x128_f8f6f4 block "
+                "note": "fp8_block_gemm with FP8BLK_GEMM_FP8_MATRIX_CORE: v_mfma_f32_32x32x64_f8f6f4 block "
                         "products, hardware-truncated inside groups of 8 (not the default path)"}
 
     out = {
@@ -607,8 +728,12 @@ def main():
                      "avg_launch_us": round(gemm_ms / n_launch * 1e3, 2),
                      "gemm_ms_per_step": round(gemm_ms, 4),
                      "gemm_ms_per_step_p10_p50_p90": [round(v, 4) for v in gemm_spread],
+                     "gemm_ms_back_to_back": round(gemm_b2b_ms, 4),
                      "note": "peak = FP8 dense MFMA (the metric's); the exact path issues F16 matrix "
-                             "instructions, whose dense peak is half of it (frac_of_issued_f16_peak)"},
+                             "instructions, whose dense peak is half of it (frac_of_issued_f16_peak); "
+                             "GEMM time per step from one event bracket around each linear's three GEMMs "
+                             "inside the step (ms_per_step itself has no event inside a step); "
+                             "gemm_ms_back_to_back sums the per-GEMM figures of `gemms`"},
         "gemms": gemms,
         "quantisers": {"ms_per_step": round(quant_ms, 4), "algorithmic_gb": round(qbytes / 1e9, 4),
                        "gbps": round(qbytes / (quant_ms * 1e-3) / 1e9, 1) if quant_ms > 0 else None,
@@ -623,6 +748,8 @@ def main():
     }
     if not args.no_sweep:
         out["cfg4_sweep"] = layer_sweep(torch, B, W, dev)
+    if not args.no_small_configs:
+        out["small_configs"] = small_configs(torch, B, W, dev)
     if not args.no_fusion:
         out["producer_fusion"] = producer_fusion(torch, B, layers, args.steps, args.warmup)
     if not args.no_layer:

@@ -361,8 +361,7 @@ def fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, dx=None, 
 def fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=None, dw=None, accumulate=False, fp8_matrix_core=False,
                          workspace=True, split2=False):
     """dW[N, K] (+)= dY^T . X from token-dimension codes dyqT [N, M_pad], xqT [K, M_pad].
-    workspace / split2: as for fp8_block_gemm (the o and down projections' weight
-    gradients are split along the tokens when a workspace is given)."""
+    workspace / split2: as for fp8_block_gemm (split2=True splits the tokens in two)."""
     _check_2d(dyqT, torch.uint8, "dyqT")
     _check_2d(xqT, torch.uint8, "xqT")
     N = dyqT.shape[0]

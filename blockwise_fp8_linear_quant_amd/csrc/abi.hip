@@ -389,7 +389,7 @@ size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
   gemm_dims(op, M, N, K, I, J, L);
   if (J % 128 != 0 || L % 128 != 0 || (op == FP8BLK_OP_WGRAD && I % 128 != 0) || !grid_fits(I, 128, J, 128))
     return 0;
-  return split_workspace_bytes(I, J, preferred_splits(I, J, L));
+  return small_split_workspace_bytes(I, J, small_grid_splits(I, J, L));
 }
 
 size_t fp8_block_gemm_split2_workspace_size(int op, int64_t M, int64_t N, int64_t K) {

@@ -148,6 +148,61 @@ __device__ __forceinline__ bool split_arrive(unsigned* counter, int t, int* flag
   return *flag != 0;
 }
 
+// The tile's value from its S partials, added in split order (split 0 +
+// split 1 + ... + split S-1) into acc, which holds this workgroup's own
+// partial (split `split`).  `first` is this lane's float of split 0 and
+// `stride` the distance between splits; partial (mt, nt, q) of a lane is the
+// float4 at ((mt * NT + nt) * 4 + q) * 256.  The loop over the splits is kept
+// rolled so that one split's loads (16 registers per sub-tile) are live at a
+// time.
+template <int S, int MT, int NT>
+__device__ __forceinline__ void add_partials(float (&acc)[MT][NT][16], const float* first, int64_t stride, int split) {
+  float tot[MT][NT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 v;
+        if (split == 0)
+          v = make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
+        else
+          v = *reinterpret_cast<const float4*>(first + ((mt * NT + nt) * 4 + q) * 256);
+        tot[mt][nt][4 * q] = v.x; tot[mt][nt][4 * q + 1] = v.y;
+        tot[mt][nt][4 * q + 2] = v.z; tot[mt][nt][4 * q + 3] = v.w;
+      }
+#pragma unroll 1
+  for (int sp = 1; sp < S; ++sp) {
+    const float* src = first + sp * stride;
+    if (sp == split) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) tot[mt][nt][e] += acc[mt][nt][e];
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(src + ((mt * NT + nt) * 4 + q) * 256);
+            tot[mt][nt][4 * q] += v.x; tot[mt][nt][4 * q + 1] += v.y;
+            tot[mt][nt][4 * q + 2] += v.z; tot[mt][nt][4 * q + 3] += v.w;
+          }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][nt][e] = tot[mt][nt][e];
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // releases global memory, which makes every wave wait for all of its
 // outstanding global loads (vmcnt(0)) -- including the direct-to-LDS fills of
@@ -331,9 +386,12 @@ struct Cfg {
 // Exact path: E4M3 -> F16 in registers, v_mfma_f32_32x32x16_f16; one
 // workgroup per output tile.
 // Split-K (S > 1): workgroup `split` of a tile contracts over scale blocks
-// [nLBtot * split / S, nLBtot * (split + 1) / S); `part` holds S FP32 partial
-// tiles per output tile, `cnt` one arrival counter per output tile.
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS, int S>
+// [nLBtot * split / S, nLBtot * (split + 1) / S).  Without PLANES, `part`
+// holds S FP32 partial tiles per output tile and `cnt` one arrival counter per
+// output tile, and the last split to arrive stores the tile; with PLANES each
+// split stores its FP32 partial into plane `split` of Cout ([S][I][ldc]) and a
+// second kernel (add_planes_kernel) adds the planes.
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS, int S, bool PLANES>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_f16_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
@@ -507,7 +565,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     }
   }
 
-  if (S > 1) {
+  if (S > 1 && !PLANES) {
     // Split-K: store this split's partial tile lane-major (one 1 KB run per
     // wave instruction); the last split to arrive adds the S partials in split
     // order -- its own from registers -- and goes on to store the tile.
@@ -522,30 +580,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
           *reinterpret_cast<float4*>(mine + ((mt * NT + nt) * 4 + q) * 256) =
               make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
     if (!split_arrive<S>(cnt + tile, t, &split_flag)) return;
-    const float* first = part + ((int64_t)tile * S * NW + wave) * kWave + lane * 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float4 sum;
-#pragma unroll
-          for (int sp = 0; sp < S; ++sp) {
-            float4 v;
-            if (sp == split)
-              v = make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
-            else
-              v = *reinterpret_cast<const float4*>(first + (int64_t)sp * NW * kWave + ((mt * NT + nt) * 4 + q) * 256);
-            if (sp == 0) {
-              sum = v;
-            } else {
-              sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-            }
-          }
-          acc[mt][nt][4 * q] = sum.x; acc[mt][nt][4 * q + 1] = sum.y;
-          acc[mt][nt][4 * q + 2] = sum.z; acc[mt][nt][4 * q + 3] = sum.w;
-        }
+    add_partials<S, MT, NT>(acc, part + ((int64_t)tile * S * NW + wave) * kWave + lane * 4, NW * kWave, split);
   }
 
   // Epilogue, one 32-row band (sub-tile row mt) at a time through LDS.  Lane l
@@ -554,6 +589,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   lds_barrier();
   {
     using Bd = Band<OUT, WN>;
+    static_assert(!PLANES || (S > 1 && OUT == OUT_F32), "partial planes are FP32");
+    // Small-grid split: this split's partial goes to plane `split` of the
+    // workspace ([S][I][ldc] FP32); add_planes_kernel adds the planes.
+    void* dst = PLANES ? static_cast<void*>(static_cast<float*>(Cout) + (int64_t)split * I * ldc) : Cout;
     uint8_t* region = band_region<32 * Bd::RS, C::kBufBytes, NS, NW>(lds0, lds1, lds2, wave);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -569,7 +608,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
             *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
           }
         }
-      store_band<OUT, WN, 32>(region, lane, Cout, ldc, i0 + wm * WM + mt * 32, j0 + wn * WN, I);
+      store_band<OUT, WN, 32>(region, lane, dst, ldc, i0 + wm * WM + mt * 32, j0 + wn * WN, I);
     }
   }
 }
@@ -577,7 +616,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
 // FP8 matrix-core path: one workgroup per output tile, the exact path's
 // pipeline with the block product formed by v_mfma_f32_32x32x64_f8f6f4 on the
 // E4M3 codes themselves (two per 32x32 sub-tile and block, no conversion).
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS, int S>
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int NW, int NS, int S, bool PLANES>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
@@ -737,7 +776,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     }
   }
 
-  if (S > 1) {
+  if (S > 1 && !PLANES) {
     // Split-K, as in the exact path: partial tiles stored lane-major, the last
     // split to arrive adds them in split order.
     constexpr int kWave = MT * NT * 16 * 64;    // floats per wave and split
@@ -751,36 +790,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
           *reinterpret_cast<float4*>(mine + ((mt * NT + nt) * 4 + q) * 256) =
               make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
     if (!split_arrive<S>(cnt + tile, t, &split_flag)) return;
-    const float* first = part + ((int64_t)tile * S * NW + wave) * kWave + lane * 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float4 sum;
-#pragma unroll
-          for (int sp = 0; sp < S; ++sp) {
-            float4 v;
-            if (sp == split)
-              v = make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
-            else
-              v = *reinterpret_cast<const float4*>(first + (int64_t)sp * NW * kWave + ((mt * NT + nt) * 4 + q) * 256);
-            if (sp == 0) {
-              sum = v;
-            } else {
-              sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-            }
-          }
-          acc[mt][nt][4 * q] = sum.x; acc[mt][nt][4 * q + 1] = sum.y;
-          acc[mt][nt][4 * q + 2] = sum.z; acc[mt][nt][4 * q + 3] = sum.w;
-        }
+    add_partials<S, MT, NT>(acc, part + ((int64_t)tile * S * NW + wave) * kWave + lane * 4, NW * kWave, split);
   }
 
   // Epilogue through LDS, one 32-row band at a time (as in the exact path).
   lds_barrier();
   {
     using Bd = Band<OUT, WN>;
+    static_assert(!PLANES || (S > 1 && OUT == OUT_F32), "partial planes are FP32");
+    // Small-grid split: this split's partial goes to plane `split` of the
+    // workspace ([S][I][ldc] FP32); add_planes_kernel adds the planes.
+    void* dst = PLANES ? static_cast<void*>(static_cast<float*>(Cout) + (int64_t)split * I * ldc) : Cout;
     uint8_t* region = band_region<32 * Bd::RS, C::kBufBytes, NS, NW>(lds0, lds1, lds2, wave);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -796,7 +816,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
             *reinterpret_cast<float4*>(pp) = make_float4(v[0], v[1], v[2], v[3]);
           }
         }
-      store_band<OUT, WN, 32>(region, lane, Cout, ldc, i0 + wm * WM + mt * 32, j0 + wn * WN, I);
+      store_band<OUT, WN, 32>(region, lane, dst, ldc, i0 + wm * WM + mt * 32, j0 + wn * WN, I);
     }
   }
 }
@@ -947,25 +967,85 @@ __global__ __launch_bounds__(256) void clear_u32_kernel(unsigned* __restrict__ p
     p[i] = 0u;
 }
 
+// Sum of the S partial planes of a small-grid split, in split order (plane 0
+// + plane 1 + ... + plane S-1), then the output epilogue: FP32, BF16 (round
+// to nearest even) or FP32 added to the values already in C.  part holds
+// [S][I][J] FP32 (plane stride I * J); one thread handles 4 consecutive
+// columns of a row, loading all S planes before adding.
+template <int OUT, int S>
+__global__ __launch_bounds__(256) void add_planes_kernel(const float* __restrict__ part, int64_t I, int64_t J,
+                                                         void* __restrict__ C, int64_t ldc) {
+  const int64_t per_row = J / 4, n = I * per_row, plane = I * J;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += (int64_t)gridDim.x * 256) {
+    const int64_t i = v / per_row, j = (v - i * per_row) * 4;
+    const float* p = part + i * J + j;
+    float4 t[S];
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) t[sp] = *reinterpret_cast<const float4*>(p + sp * plane);
+    float4 sum = t[0];
+#pragma unroll
+    for (int sp = 1; sp < S; ++sp) {
+      sum.x += t[sp].x; sum.y += t[sp].y; sum.z += t[sp].z; sum.w += t[sp].w;
+    }
+    if (OUT == OUT_BF16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + i * ldc + j) =
+          make_uint2(bf16x2(sum.x, sum.y), bf16x2(sum.z, sum.w));
+    } else {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(C) + i * ldc + j);
+      if (OUT == OUT_F32_ACC) {
+        const float4 old = *dst;
+        sum.x += old.x; sum.y += old.y; sum.z += old.z; sum.w += old.w;
+      }
+      *dst = sum;
+    }
+  }
+}
+
 constexpr int kCUs = 256;   // MI355X compute units
 
-template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS, int S>
+template <int BM, int BN, int WM, int WN, int SB_MODE, int OUT, int PREC, int NW, int NS, int S, bool PLANES = false>
 void launch_cfg(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                 const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
                 int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, float* part, unsigned* cnt, hipStream_t st) {
   const int tilesM = (int)((I + BM - 1) / BM), tilesN = (int)(J / BN);
   const int nUnits = tilesM * tilesN * S;
   if (PREC == PREC_F16) {
-    hipLaunchKernelGGL((block_gemm_f16_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS, S>), dim3(nUnits), dim3(64 * NW),
+    hipLaunchKernelGGL((block_gemm_f16_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS, S, PLANES>), dim3(nUnits), dim3(64 * NW),
                        0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN, part, cnt);
   } else {
-    hipLaunchKernelGGL((block_gemm_fp8_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS, S>), dim3(nUnits), dim3(64 * NW),
+    hipLaunchKernelGGL((block_gemm_fp8_kernel<BM, BN, WM, WN, SB_MODE, OUT, NW, NS, S, PLANES>), dim3(nUnits), dim3(64 * NW),
                        0, st, A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN, part, cnt);
   }
 }
 
-// Tile choice: with a split plan, 256 x 128 tiles split in two along the
-// contraction; otherwise 256 x 128 output tiles (8 waves of 64 x 64,
+// Small-grid split: S kernels' worth of partial planes from one launch of
+// 128 x 128 tiles x S splits, then add_planes_kernel.
+template <int SB_MODE, int OUT, int PREC, int S>
+void launch_planes_s(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
+                     const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
+                     int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, float* part, hipStream_t st) {
+  launch_cfg<128, 128, 64, 64, SB_MODE, OUT_F32, PREC, 4, 2, S, true>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L,
+                                                                      part, J, nullptr, nullptr, st);
+  const int64_t n = I * (J / 4);
+  const unsigned blocks = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  hipLaunchKernelGGL((add_planes_kernel<OUT, S>), dim3(blocks), dim3(256), 0, st, part, I, J, C, ldc);
+}
+
+template <int SB_MODE, int OUT, int PREC>
+void launch_planes(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
+                   const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
+                   int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, const SplitPlan& plan, hipStream_t st) {
+  if (plan.splits == 2)
+    launch_planes_s<SB_MODE, OUT, PREC, 2>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, plan.part, st);
+  else if (plan.splits == 4)
+    launch_planes_s<SB_MODE, OUT, PREC, 4>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, plan.part, st);
+  else
+    launch_planes_s<SB_MODE, OUT, PREC, 8>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, plan.part, st);
+}
+
+// Tile choice: a split plan runs the split on 256 x 128 tiles (split in two,
+// FP8BLK_GEMM_SPLIT2) or on 128 x 128 tiles into partial planes (split 2, 4 or
+// 8 ways, the default for small grids); otherwise 256 x 128 output tiles (8 waves of 64 x 64,
 // triple-buffered LDS, one workgroup per CU) when they fill every CU for a
 // whole number of rounds, else 128 x 128 tiles (4 waves, double-buffered, two
 // workgroups per CU), whose finer granularity keeps every CU busy in a partial
@@ -974,9 +1054,11 @@ template <int SB_MODE, int OUT, int PREC>
 void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                  const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
                  int64_t I, int64_t J, int64_t L, void* C, int64_t ldc, const SplitPlan& plan, hipStream_t st) {
-  if (plan.splits == 2)
+  if (plan.splits > 1 && plan.split_big_tiles)
     launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3, 2>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc,
                                                               plan.part, plan.counters, st);
+  else if (plan.splits > 1)
+    launch_planes<SB_MODE, OUT, PREC>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc, plan, st);
   else if (plan.big_tiles)
     launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3, 1>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc,
                                                               nullptr, nullptr, st);
@@ -1001,12 +1083,16 @@ void launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
 
 }  // namespace
 
-// Workspace layout of a split plan: a fixed 64 KiB region of 4-byte arrival
-// counters (one per output tile, so at most kMaxSplitTiles tiles are split),
-// then S FP32 partial tiles of 256 x 128 per output tile.  The counter region
-// does not depend on the shape, so one workspace can serve problems of
-// different shapes in turn: no problem's partial tiles ever overlap another
-// problem's counters, and every call leaves the counters it used at zero.
+// Workspace layout of the split in two (FP8BLK_GEMM_SPLIT2): a fixed 64 KiB
+// region of 4-byte arrival counters (one per output tile, so at most
+// kMaxSplitTiles tiles are split), then two FP32 partial tiles of 256 x 128
+// per output tile.  The counter region does not depend on the shape, so one
+// workspace can serve problems of different shapes in turn: no problem's
+// partial tiles ever overlap another problem's counters, and every call leaves
+// the counters it used at zero.  The small-grid split needs no counters; it
+// leaves the counter region untouched and puts S FP32 partial planes of the
+// I x J output after it, so a workspace whose counters are zero stays valid for
+// either plan in any order.
 constexpr int64_t kCounterBytes = 64 * 1024;
 constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
 
@@ -1017,28 +1103,53 @@ size_t split_workspace_bytes(int64_t I, int64_t J, int splits) {
   return (size_t)kCounterBytes + (size_t)tiles * splits * 256 * 128 * 4;
 }
 
-// The split a problem uses by default: none.  Splitting the contraction in two
-// (partial tiles in the workspace, added by the second split to finish) was
-// measured on the layer's under-filled shapes -- the o and down weight
+// The split a problem uses by default, given room for it in the workspace.
+// Grids of at most kCUs / 4 output tiles of 128 x 128 (e.g. a 256-token
+// forward GEMM into 2048 features: 32 tiles, each contracting 16 scale blocks
+// on a CU of its own while 224 CUs idle) are split along the contraction into
+// S = 8, 4 or 2: the largest S with S * tiles <= kCUs and at least two scale
+// blocks per split.  The splits write FP32 partial planes and a second kernel
+// adds them in split order (an in-kernel last-arriver sum was slower here:
+// each workgroup's agent-scope release writes back its XCD's L2, and the last
+// split read the other seven partial tiles on its own).  Larger grids are not
+// split: splitting the contraction in
+// two was measured on the layer's under-filled shapes -- the o and down weight
 // gradients, 128 and 384 tiles of 256 x 128 -- and was slower than the
 // unsplit kernels there (59 against 50 us and 160 against 128 us at 4096
 // tokens): each split pays the tile prologue and epilogue, the partial tiles'
-// round trip and one L2 write-back, more than the fuller CUs gain.  Splitting
-// stays available on request (FP8BLK_GEMM_SPLIT2).
-int preferred_splits(int64_t I, int64_t J, int64_t L) {
-  (void)I; (void)J; (void)L;
-  return 1;
+// round trip and one L2 write-back, more than the fuller CUs gain.  The split
+// in two on 256 x 128 tiles stays available on request (FP8BLK_GEMM_SPLIT2).
+int small_grid_splits(int64_t I, int64_t J, int64_t L) {
+  const int64_t tiles = ((I + 127) / 128) * (J / 128);
+  const int64_t nLB = L / 128;
+  if (tiles > kCUs / 4) return 1;
+  int s = 8;
+  while (s > 1 && (tiles * s > kCUs || nLB < 2 * s)) s /= 2;
+  return s;
+}
+
+size_t small_split_workspace_bytes(int64_t I, int64_t J, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)kCounterBytes + (size_t)splits * (size_t)I * (size_t)J * 4;
 }
 
 SplitPlan plan_split(int64_t I, int64_t J, int64_t L, void* ws, size_t ws_bytes, bool force) {
   SplitPlan p;
   const int64_t big = ((I + 255) / 256) * (J / 128);
   p.big_tiles = big >= kCUs && big % kCUs == 0;
-  const int want = force ? (L / 128 >= 2 ? 2 : 1) : preferred_splits(I, J, L);
-  const size_t need = split_workspace_bytes(I, J, 2);
-  if (want == 2 && need > 0 && ws != nullptr && ws_bytes >= need) {
-    p.splits = 2;
-    p.counters = static_cast<unsigned*>(ws);
+  if (force) {
+    const size_t need = split_workspace_bytes(I, J, 2);
+    if (L / 128 >= 2 && need > 0 && ws != nullptr && ws_bytes >= need) {
+      p.splits = 2;
+      p.split_big_tiles = true;
+    }
+  } else {
+    const int s = small_grid_splits(I, J, L);
+    const size_t need = small_split_workspace_bytes(I, J, s);
+    if (s > 1 && need > 0 && ws != nullptr && ws_bytes >= need) p.splits = s;
+  }
+  if (p.splits > 1) {
+    p.counters = p.split_big_tiles ? static_cast<unsigned*>(ws) : nullptr;
     p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
   }
   return p;

@@ -32,20 +32,26 @@ enum SbMode { SB_BLOCK = 0, SB_ROWS = 1 };
 enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_F32_ACC = 2 };
 
 // How a block GEMM is laid out over the CUs: 256 x 128 tiles or 128 x 128
-// tiles, and, with a workspace, 256 x 128 tiles split in two along the
-// contraction (counters and partial tiles in the workspace).
+// tiles; with a workspace, 256 x 128 tiles split in two along the contraction
+// (on request) or 128 x 128 tiles split 2, 4 or 8 ways (small grids), with
+// counters and partial tiles in the workspace.
 struct SplitPlan {
-  bool big_tiles = false;
+  bool big_tiles = false;        // unsplit: 256 x 128 tiles (else 128 x 128)
   int splits = 1;
+  bool split_big_tiles = false;  // split: 256 x 128 tiles (else 128 x 128)
   unsigned* counters = nullptr;
   float* part = nullptr;
 };
-// Workspace bytes for `splits` splits of an I x J output (0 for one split).
+// Workspace bytes for `splits` splits of an I x J output on 256 x 128 tiles
+// (0 for one split).
 size_t split_workspace_bytes(int64_t I, int64_t J, int splits);
-// The split count the launch policy picks for I x J x L given room for it.
-int preferred_splits(int64_t I, int64_t J, int64_t L);
-// The plan for a call: split in two when preferred (or forced) and the
-// workspace holds split_workspace_bytes(I, J, 2); otherwise one split.
+// The default split of I x J x L (1, 2, 4 or 8; see gemm.hip) and its
+// workspace bytes on 128 x 128 tiles.
+int small_grid_splits(int64_t I, int64_t J, int64_t L);
+size_t small_split_workspace_bytes(int64_t I, int64_t J, int splits);
+// The plan for a call: with `force`, split in two on 256 x 128 tiles when the
+// workspace holds split_workspace_bytes(I, J, 2); otherwise the default split
+// when the workspace holds its bytes; else one split.
 SplitPlan plan_split(int64_t I, int64_t J, int64_t L, void* ws, size_t ws_bytes, bool force);
 
 // C[I, J] = sum_lb SA(i, lb) SB(j, lb) sum_{l in lb} A[i, l] B[j, l]

@@ -51,19 +51,41 @@ def test_status_strings_and_version():
 
 
 def test_workspace_sizes():
-    """No shape is split by default (workspace size 0); the forced split needs a fixed
-    64 KiB counter region plus two FP32 partial tiles of 256 x 128 per output tile."""
+    """The layer's shapes are not split by default (workspace size 0); grids of at most
+    64 output tiles of 128 x 128 are split 8, 4 or 2 ways (the largest split with at most
+    256 workgroups and two scale blocks per split), which needs a 64 KiB region it
+    leaves alone (the other plan's counters) plus S FP32 partial planes of the I x J
+    output.  The forced split needs a 64 KiB counter region plus two FP32
+    partial tiles of 256 x 128 per output tile."""
     lib = _lib()
     FWD, DGRAD, WGRAD = 0, 1, 2
     size, size2 = lib.fp8_block_gemm_workspace_size, lib.fp8_block_gemm_split2_workspace_size
     tiles = lambda I, J: ((I + 255) // 256) * (J // 128)
     need = lambda I, J: 65536 + tiles(I, J) * 2 * 256 * 128 * 4
+    out_dims = {FWD: lambda M, N, K: (M, N), DGRAD: lambda M, N, K: (M, K), WGRAD: lambda M, N, K: (N, K)}
+    small = lambda op, M, N, K, s: 65536 + s * 4 * out_dims[op](M, N, K)[0] * out_dims[op](M, N, K)[1]
     for n, k in ((4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144)):
         for op in (FWD, DGRAD, WGRAD):
             assert size(op, 4096, n, k) == 0
+            assert size(op, 8192, n, k) == 0
         assert size2(FWD, 4096, n, k) == need(4096, n)
         assert size2(DGRAD, 4096, n, k) == need(4096, k)
         assert size2(WGRAD, 4096, n, k) == need(n, k)
+    # Small grids: (op, M, N, K) -> (output tiles of 128 x 128, splits).
+    for op, M, N, K, t, s in ((FWD, 256, 2048, 2048, 32, 8),     # 16 scale blocks
+                              (DGRAD, 256, 2048, 2048, 32, 8),
+                              (FWD, 256, 2048, 2304, 32, 8),     # 18 blocks: splits of 2 and 3
+                              (DGRAD, 256, 2048, 2304, 36, 4),   # 36 tiles: 8 splits would pass 256
+                              (FWD, 300, 1024, 1024, 24, 4),     # 8 blocks
+                              (FWD, 512, 2048, 2048, 64, 4),     # 64 tiles: the largest split grid
+                              (FWD, 300, 256, 512, 6, 2),        # 4 blocks
+                              (FWD, 1000, 128, 640, 8, 2),       # 5 blocks: splits of 2 and 3
+                              (WGRAD, 2048, 256, 1024, 16, 8),   # 16 token blocks
+                              (WGRAD, 1000, 128, 640, 5, 4)):    # 1000 tokens pad to 8 blocks
+        assert size(op, M, N, K) == small(op, M, N, K, s), (op, M, N, K, t)
+    assert size(FWD, 640, 1664, 2048) == 0        # 65 tiles
+    assert size(FWD, 300, 256, 384) == 0          # 3 blocks: fewer than two per split
+    assert size(WGRAD, 256, 2048, 2048) == 0      # 256 tiles
     assert size2(WGRAD, 4096, 2048, 2048) == 65536 + 128 * 2 * 256 * 128 * 4    # 128 tiles: 32 MiB + counters
     assert size2(FWD, 300, 256, 384) == 65536 + 4 * 2 * 256 * 128 * 4           # 2 x 2 tiles
     # More than 16384 output tiles (the counter region's capacity): never split.

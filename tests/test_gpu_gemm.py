@@ -511,3 +511,115 @@ def test_split_k_deterministic_and_counters_left_zero(B):
                   "split wgrad o", rng, k=32)
     check_sampled(c, lambda r=None, cc=None: gemm.wgrad(odyqT, osdyT, oxqT, osxT, r, cc), "f32",
                   "unsplit wgrad o", rng, k=32)
+
+
+# (M, N, K) and the default split of the forward, data-gradient and weight-gradient
+# GEMMs (1: unsplit).  The launch rule: an output of at most 64 tiles of 128 x 128
+# is split along the contraction into the largest S of 8, 4 and 2 with S * tiles <= 256
+# and at least two scale blocks per split, when the workspace holds S FP32 partial planes
+# of the output (summed in split order by a second kernel).
+SMALL_GRIDS = [((256, 2048, 2048), (8, 8, 1)),      # configuration 1's shape
+               ((256, 2048, 2304), (8, 4, 1)),      # 18 blocks over 8 splits: 2 or 3 each
+               ((300, 1024, 1024), (4, 4, 1)),
+               ((1000, 128, 640), (2, 1, 4)),       # 5 blocks over 2 splits; 1000 tokens pad to 8 blocks
+               ((2048, 256, 1024), (4, 1, 8))]
+
+
+def _small_split_bytes(op, M, N, K, s):
+    """The 64 KiB counter region (left alone) and S FP32 partial planes of the I x J
+    output (0 when not split)."""
+    I, J = {0: (M, N), 1: (M, K), 2: (N, K)}[op]
+    return 0 if s == 1 else 65536 + s * I * J * 4
+
+
+@pytest.mark.parametrize("shape,splits", SMALL_GRIDS)
+@pytest.mark.parametrize("mc", [False, True])
+def test_small_grid_split(B, shape, splits, mc):
+    """Small grids split along the contraction by default (binding workspace): every
+    element of the forward (FP32 and BF16), data gradient and weight gradient (overwrite
+    and accumulate) against the oracle, on both matrix paths."""
+    torch = _torch()
+    M, N, K = shape
+    for op, s in zip((B.OP_FWD, B.OP_DGRAD, B.OP_WGRAD), splits):
+        assert B.fp8_block_gemm_workspace_size(op, M, N, K) == _small_split_bytes(op, M, N, K, s), (op, s)
+    L = _split_layer(B, M, N, K, 11 * M + N)
+    rtol = 2.0 ** -10 + 1e-5 if mc else compare.FP32_RTOL
+    xq, sx, xqT, sxT = B.fp8_quant_1x128_dual(L.x)
+    wq, sw, wqT, swT = B.fp8_quant_128x128(L.w, with_transpose=True)
+    dyq, sdy, dyqT, sdyT = B.fp8_quant_1x128_dual(L.dy)
+    oxq, osx = quant.quant_1x128_rows(L.xb)
+    owq, osw = quant.quant_128x128(L.wb)
+    for od, out in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+        say("small-grid split fwd", out, mc, shape, splits[0])
+        y = host(B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=od, fp8_matrix_core=mc))
+        yr, bnd = gemm.fwd(oxq, osx, owq, osw)
+        ok, rep = (compare.check_fp32(y, yr, bnd, rtol=rtol) if out == "f32"
+                   else compare.check_bf16(y, yr, bnd, rtol=rtol))
+        assert ok, ("fwd", out, rep)
+    say("small-grid split dgrad", mc, shape, splits[1])
+    odyq, osdy = quant.quant_1x128_rows(L.dyb)
+    owqT, oswT = quant.quant_128x128(np.ascontiguousarray(L.wb.T))
+    dx = host(B.fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.bfloat16, fp8_matrix_core=mc))
+    yr, bnd = gemm.dgrad(odyq, osdy, owqT, oswT)
+    ok, rep = compare.check_bf16(dx, yr, bnd, rtol=rtol)
+    assert ok, ("dgrad", rep)
+    say("small-grid split wgrad", mc, shape, splits[2])
+    odyqT, osdyT = quant.quant_1x128_tokens(L.dyb)
+    oxqT, osxT = quant.quant_1x128_tokens(L.xb)
+    yr, bnd = gemm.wgrad(odyqT, osdyT, oxqT, osxT)
+    dw = host(B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, fp8_matrix_core=mc))
+    ok, rep = compare.check_fp32(dw, yr, bnd, rtol=rtol)
+    assert ok, ("wgrad", rep)
+    dw0 = np.random.default_rng(M + 3).standard_normal((N, K)).astype(np.float32) * 1e-3
+    dwt = torch.from_numpy(dw0).cuda()
+    B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, dw=dwt, accumulate=True, fp8_matrix_core=mc)
+    ok, rep = compare.check_fp32(host(dwt), yr + dw0.astype(np.float64),
+                                 bnd + np.abs(dw0) * (2.0 ** -23 / compare.FP32_RTOL), rtol=rtol)
+    assert ok, ("wgrad accumulate", rep)
+
+
+@pytest.mark.parametrize("mc", [False, True])
+def test_small_grid_split_deterministic_and_counters_left_zero(B, mc):
+    """Configuration 1's forward GEMM split 8 ways with a caller-owned workspace: two
+    calls give identical bits, the counter region of the split in two stays zero,
+    stale partial planes do not matter, a workspace one byte short runs unsplit, and
+    the unsplit result meets the same rule."""
+    torch = _torch()
+    M, N, K = 256, 2048, 2048
+    L = _split_layer(B, M, N, K, 5)
+    xq, sx = B.fp8_quant_1x128(L.x)
+    wq, sw, _, _ = B.fp8_quant_128x128(L.w)
+    need = B.fp8_block_gemm_workspace_size(B.OP_FWD, M, N, K)
+    assert need == _small_split_bytes(0, M, N, K, 8)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    say("small-grid split determinism", mc)
+    a = B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.float32, fp8_matrix_core=mc, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0     # the counter region is left alone
+    ws[65536:].fill_(0x7F)
+    b = B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.float32, fp8_matrix_core=mc, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    # One byte short of the planes: the call runs unsplit.
+    short = torch.zeros(need - 1, dtype=torch.uint8, device="cuda")
+    d = B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.float32, fp8_matrix_core=mc, workspace=short)
+    c = host(B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.float32, fp8_matrix_core=mc, workspace=False))
+    yr, bnd = gemm.fwd(*quant.quant_1x128_rows(L.xb), *quant.quant_128x128(L.wb))
+    rtol = 2.0 ** -10 + 1e-5 if mc else compare.FP32_RTOL
+    assert torch.equal(torch.from_numpy(c).view(torch.int32), d.cpu().view(torch.int32))
+    for got, what in ((host(a), "split"), (c, "unsplit")):
+        ok, rep = compare.check_fp32(got, yr, bnd, rtol=rtol)
+        assert ok, (what, rep)
+    # The same workspace then serves the split in two (FP8BLK_GEMM_SPLIT2), whose
+    # arrival counters the plane split must have left at zero.
+    L2 = _split_layer(B, 300, 256, 384, 6)
+    x2q, s2x = B.fp8_quant_1x128(L2.x)
+    w2q, s2w, _, _ = B.fp8_quant_128x128(L2.w)
+    assert B.fp8_block_gemm_split2_workspace_size(B.OP_FWD, 300, 256, 384) <= need
+    y2 = B.fp8_block_gemm_fwd(x2q, s2x, w2q, s2w, out_dtype=torch.float32, fp8_matrix_core=mc, workspace=ws,
+                              split2=True)
+    torch.cuda.synchronize()
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+    yr2, bnd2 = gemm.fwd(*quant.quant_1x128_rows(L2.xb), *quant.quant_128x128(L2.wb))
+    ok, rep = compare.check_fp32(host(y2), yr2, bnd2, rtol=rtol)
+    assert ok, ("split in two after the plane split", rep)
