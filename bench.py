@@ -18,7 +18,10 @@ about 5 us).  `roofline` covers the dominant kernel (the block GEMM), timed in a
 second pass of K steps with one event bracket around each linear's three GEMMs
 on the stream the kernels run on; its `frac` is taken against the FP8 dense
 MFMA peak, the metric's own.  Per-GEMM figures come from K back-to-back
-launches of each GEMM.  `cpu_baseline` times the numpy oracle on a bounded token
+launches of each GEMM.  Before the W warm-up steps, untimed steps run for
+--clock-warmup-s seconds (default 0.5): the GPU idles during the host-side
+setup, and a timed region that starts before its clock has settled reads about
+3% slow.  `cpu_baseline` times the numpy oracle on a bounded token
 sample of the same layer with all host threads, and on the same sample with
 one thread (`single_thread`), quantisers (GB/s) and GEMMs (TFLOP/s) apart.
 """
@@ -55,6 +58,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the 28-layer M=8192 sweep")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole decoder layer fwd+bwd")
     ap.add_argument("--no-small-configs", action="store_true", help="skip the kernel-by-kernel timing of configurations 1 and 5")
+    ap.add_argument("--clock-warmup-s", type=float, default=0.5,
+                    help="untimed steps for this many seconds before the warm-up steps, so that the timed "
+                         "region starts at the GPU's steady-state clock")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -606,10 +612,14 @@ def main():
            linear's quantisers and one around its three GEMMs, with the p10/p50/p90
            of the GEMM time over the steps;
         3. ms of each GEMM [linear][op], from K launches of it back to back
-           between two events.
+           between two events (back_to_back).
         Returns (ms/step, GEMM ms/step, per-GEMM ms, quantiser ms/step, wall s of
         pass 1, GEMM spread)."""
         mk = lambda: torch.cuda.Event(enable_timing=True)
+        t_end = time.perf_counter() + args.clock_warmup_s
+        while time.perf_counter() < t_end:
+            step(fp8_mc)
+            torch.cuda.synchronize()
         for _ in range(args.warmup):
             step(fp8_mc)
         torch.cuda.synchronize()
@@ -634,21 +644,22 @@ def main():
                        for s in range(args.steps) for i in range(len(layers))) / args.steps
         pct = lambda q: gemm_steps[min(len(gemm_steps) - 1, int(q * (len(gemm_steps) - 1) + 0.5))]
 
-        per_gemm = []
-        for L in layers:
-            row = []
-            for f in L.gemm_calls(B, fp8_mc):
-                f()
-                torch.cuda.synchronize()
-                e0, e1 = mk(), mk()
-                e0.record()
-                for _ in range(args.steps):
-                    f()
-                e1.record()
-                torch.cuda.synchronize()
-                row.append(e0.elapsed_time(e1) / args.steps)
-            per_gemm.append(row)
+        per_gemm = [[back_to_back(f) for f in L.gemm_calls(B, fp8_mc)] for L in layers]
         return ms_step, gemm_ms, per_gemm, quant_ms, t_wall, [pct(0.1), pct(0.5), pct(0.9)]
+
+    def back_to_back(f):
+        """ms of one launch of f: K launches between two events, queued behind a spin
+        kernel so that the GPU never waits for Python to issue the next launch."""
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(4_000_000)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
 
     # Timed region (default path: exact block products on the F16 matrix path).
     ms_step, gemm_ms, per_gemm, quant_ms, t_wall, gemm_spread = timed(False)
@@ -664,6 +675,14 @@ def main():
         for op, ms, fl in zip(("fwd", "dgrad", "wgrad"), row, L.gemm_flops()):
             gemms[f"{op}_{L.name}"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
     qbytes = sum(L.quant_bytes() for L in layers)
+    quant_kernels = {}
+    for L in layers:
+        calls = {"dual_x": lambda: B.fp8_quant_1x128_dual(L.x, L.xq, L.sx, L.xqT, L.sxT),
+                 "blocks_w": lambda: B.fp8_quant_128x128(L.w, True, L.wq, L.sw, L.wqT, L.swT),
+                 "dual_dy": lambda: B.fp8_quant_1x128_dual(L.dy, L.dyq, L.sdy, L.dyqT, L.sdyT)}
+        for name, f in calls.items():
+            quant_kernels[f"{name}_{L.name}"] = back_to_back(f)
+    quant_b2b_ms = sum(quant_kernels.values())
 
     # The same quantiser outputs from the separate row-wise and token-dimension
     # kernels (two reads of X and dY), for comparison with the single-read path.
@@ -740,10 +759,18 @@ def main():
                        "frac_hbm_peak": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                        if quant_ms > 0 else None,
                        "path": "single-read dual 1x128 quantiser for X and dY + 128x128 for W",
+                       "timing": "ms_per_step: one event bracket around each linear's three quantisers inside "
+                                 "the step (each bracket adds about 5 us); back_to_back: each quantiser launched "
+                                 "K times in a row behind a queued spin kernel (GPU time only)",
+                       "back_to_back": {"ms_per_step": round(quant_b2b_ms, 4),
+                                        "gbps": round(qbytes / (quant_b2b_ms * 1e-3) / 1e9, 1),
+                                        "frac_hbm_peak": round(qbytes / (quant_b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                        "kernel_us": {k: round(v * 1e3, 2) for k, v in quant_kernels.items()}},
                        "separate_kernels": {"ms_per_step": round(sep_ms, 4), "algorithmic_gb": round(sep_bytes / 1e9, 4),
                                             "gbps": round(sep_bytes / (sep_ms * 1e-3) / 1e9, 1)},
                        "cold_inputs": cold},
         "wall_s_timed": round(t_wall, 3),
+        "clock_warmup_s": args.clock_warmup_s,
         "fp8_matrix_core_path": fast,
     }
     if not args.no_sweep:
