@@ -133,6 +133,45 @@ FP8BLK_HD float group_quotient(float x, const GroupQ& g) {
   return fmaf(-en, g.r_n, q0);
 }
 
+// Two-operation form of the same quotient, for groups whose reciprocal is a
+// finite binary32 (every BF16 group maximum from about 1.3e-36 up).  With the
+// reciprocal split into a double word,
+//     rhi = 1 / s rounded down,   rlo = fl32((1 - s * rhi) * rhi) >= 0
+// (the residual 1 - s * rhi is exact by FMA, and non-negative because rhi is
+// rounded down), the quotient is
+//     q = fl32(x * rhi + fl32(x * rlo))          (one multiply, one FMA),
+// which carries an error of a few 2^-48 relative before its single rounding;
+// rlo >= 0 keeps the sign of a zero x.  It yields the same E4M3 code as
+// E4M3(fl32(x / s)) for every pair of BF16 values with |x| <= amax, both
+// signs (checked exhaustively on the host, with the constants formed exactly
+// as here from the table-driven setup); the binary32 quotient itself may
+// differ in its last place where the code cannot.  Zero groups get
+// rhi = rlo = 0 (their codes are forced to 0x00 by the caller).
+struct GroupQ2 {
+  float rhi;
+  float rlo;
+};
+
+// The two-operation constants of group g; false if 1 / s overflows binary32,
+// in which case the caller must use group_quotient.
+FP8BLK_HD bool group_setup2(const GroupQ& g, GroupQ2& o) {
+  o.rhi = 0.0f;
+  o.rlo = 0.0f;
+  if (g.s == 0.0f) return true;
+  // fl32(1 / s) = 2^k * fl32(1 / s_n) exactly: the scaling is by a power of
+  // two and the result is a normal binary32 (or overflows to infinity).
+  float rhi = ldexpf(g.r_n, g.k);
+  if (!(rhi <= 3.4028234663852886e38f)) return false;
+  // Round down: if fl32(1 / s) rounded up (negative residual), step to the
+  // binary32 below it (rhi is a positive normal, so its bit pattern minus one).
+  if (fmaf(-g.s, rhi, 1.0f) < 0.0f) rhi = bits_f32(f32_bits(rhi) - 1u);
+  o.rhi = rhi;
+  o.rlo = fmaf(-g.s, rhi, 1.0f) * rhi;
+  return true;
+}
+
+FP8BLK_HD float group_quotient2(float x, const GroupQ2& g) { return fmaf(x, g.rhi, x * g.rlo); }
+
 // binary32 -> OCP E4M3 code (low 8 bits), RNE, saturating, sign kept.
 FP8BLK_HD uint32_t e4m3_encode(float q) {
   uint32_t u = f32_bits(q);

@@ -74,6 +74,14 @@ __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
 __device__ __forceinline__ uint32_t code4(float a, float b, float c, float d, const GroupQ& g) {
   return enc4(group_quotient(a, g), group_quotient(b, g), group_quotient(c, g), group_quotient(d, g));
 }
+// The same with the two-operation quotient (groups whose reciprocal is finite).
+__device__ __forceinline__ uint32_t code4(float a, float b, float c, float d, const GroupQ2& g) {
+  return enc4(group_quotient2(a, g), group_quotient2(b, g), group_quotient2(c, g), group_quotient2(d, g));
+}
+
+// True in every lane if every active lane's flag is true (a wave vote, so a
+// branch on it is uniform).
+__device__ __forceinline__ bool wave_all(bool v) { return __all(v ? 1 : 0) != 0; }
 
 // Any binary32 -> E4M3 code: hardware below 464, saturation at and above it
 // (infinities included), and S.1111.111 (0x7F with the sign) for NaN.
@@ -177,10 +185,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   amax = max8(amax);
 
   const GroupQ gq = group_setup(amax);
+  GroupQ2 g2;
+  const bool fast = wave_all(group_setup2(gq, g2));
   const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;   // zero group -> codes 0x00
   uint32_t w[4];
+  if (fast) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d) w[d] = keep & code4(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], gq);
+    for (int d = 0; d < 4; ++d) w[d] = keep & code4(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], g2);
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w[d] = keep & code4(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], gq);
+  }
   if (row_ok) {
     uint8_t* qr = q + row * ldq;
     if (col0 < C) store8(qr + col0, col0, C, w[0], w[1]);
@@ -226,17 +241,37 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
     m = fmaxf(m, __shfl_xor(m, 32));
     am[j] = m;
   }
+  // Two-operation constants and scales of the 8 groups; the normalised
+  // constants are formed again only if some group of the wave needs them.
+  GroupQ2 g2[8];
+  float sc[8];
+  bool ok = true;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const GroupQ gq = group_setup(am[j]);
-    const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
-    uint32_t w[4];
+    ok = group_setup2(gq, g2[j]) && ok;
+    sc[j] = gq.s;
+  }
+  const bool fast = wave_all(ok);
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-      w[d] = keep & code4(elem(v[4 * d], j), elem(v[4 * d + 1], j), elem(v[4 * d + 2], j), elem(v[4 * d + 3], j), gq);
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t keep = (sc[j] == 0.0f) ? 0u : 0xffffffffu;
+    uint32_t w[4];
+    if (fast) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        w[d] = keep & code4(elem(v[4 * d], j), elem(v[4 * d + 1], j), elem(v[4 * d + 2], j), elem(v[4 * d + 3], j),
+                            g2[j]);
+    } else {
+      const GroupQ gq = group_setup(am[j]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        w[d] = keep & code4(elem(v[4 * d], j), elem(v[4 * d + 1], j), elem(v[4 * d + 2], j), elem(v[4 * d + 3], j),
+                            gq);
+    }
     if (f0 + j < C) {
       *reinterpret_cast<uint4*>(qT + (f0 + j) * ldq + t0) = make_uint4(w[0], w[1], w[2], w[3]);
-      if (b == 0) s[tg * lds + f0 + j] = gq.s;
+      if (b == 0) s[tg * lds + f0 + j] = sc[j];
     }
   }
 }
@@ -278,15 +313,26 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
   const GroupQ gq = group_setup(m);
+  GroupQ2 g2;
+  const bool fast = group_setup2(gq, g2);   // one group per workgroup: uniform
   const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
   // Row-major codes: rw[i][0] = columns 0..3 of row i, rw[i][1] = columns 4..7.
   uint32_t rw[8][2];
+  if (fast) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      rw[i][hh] = keep & code4(elem(v[i], 4 * hh), elem(v[i], 4 * hh + 1), elem(v[i], 4 * hh + 2),
-                               elem(v[i], 4 * hh + 3), gq);
+      for (int hh = 0; hh < 2; ++hh)
+        rw[i][hh] = keep & code4(elem(v[i], 4 * hh), elem(v[i], 4 * hh + 1), elem(v[i], 4 * hh + 2),
+                                 elem(v[i], 4 * hh + 3), g2);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        rw[i][hh] = keep & code4(elem(v[i], 4 * hh), elem(v[i], 4 * hh + 1), elem(v[i], 4 * hh + 2),
+                                 elem(v[i], 4 * hh + 3), gq);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     if (r0 + i < R && c0 < C) store8(q + (r0 + i) * ldq + c0, c0, C, rw[i][0], rw[i][1]);
@@ -345,6 +391,11 @@ __device__ __forceinline__ uint32_t code4_each(float a, float b, float c, float 
   // elements, so its quotients are +-0; the caller masks those bytes to 0x00.
   return enc4(group_quotient(a, g[j0 + 0]), group_quotient(b, g[j0 + 1]), group_quotient(c, g[j0 + 2]),
               group_quotient(d, g[j0 + 3]));
+}
+// The same with the two-operation quotient (zero column groups: rhi = rlo = 0).
+__device__ __forceinline__ uint32_t code4_each(float a, float b, float c, float d, const GroupQ2 (&g)[8], int j0) {
+  return enc4(group_quotient2(a, g[j0 + 0]), group_quotient2(b, g[j0 + 1]), group_quotient2(c, g[j0 + 2]),
+              group_quotient2(d, g[j0 + 3]));
 }
 
 // Element sources of the dual quantiser: eight BF16 values (bit patterns) of
@@ -420,7 +471,8 @@ __device__ __forceinline__ void dual_encode(
     const uint4 (&v)[8], int64_t br, int64_t bc, int64_t R, int64_t C,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
-    float (*cred)[128], const SetupEntry* stab, uint4* stage, float4* rowq, float4* colq) {
+    float (*cred)[128], const SetupEntry* stab, uint4* stage, float4* rowq, float4* colq,
+    float4* rowq2, float4* colq2, int* tiny) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
@@ -459,50 +511,86 @@ __device__ __forceinline__ void dual_encode(
   // Group constants are set up once per group and shared through LDS (each
   // thread would otherwise set up all 16 of its groups): lane c < 8 of each
   // DPP row sets up row r0 + c (all 16 lanes hold the 8 row maxima) and
-  // stores its scale, thread t < 128 does the same for column t.  Both tables
+  // stores its scale, thread t < 128 does the same for column t.  The tables
   // are index-major (rowq[i][rb], colq[j][c]): the 16 lanes of a read either
   // share one row entry or take 16 consecutive column entries, free of bank
-  // conflicts.
+  // conflicts.  rowq2/colq2 hold the two-operation constants {rhi, rlo, s};
+  // a group whose reciprocal overflows sets *tiny, and the whole tile then
+  // takes the normalised quotient from rowq/colq {s_n, r_n, k, s}.
   {
     float m = rm[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) m = (c == i) ? rm[i] : m;
     if (c < 8) {
       const GroupQ g = group_setup_bf16(m, stab);
+      GroupQ2 g2;
+      if (!group_setup2(g, g2)) *tiny = 1;
       rowq[c * 16 + rb] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
+      rowq2[c * 16 + rb] = make_float4(g2.rhi, g2.rlo, g.s, 0.0f);
       if (FULL || r0 + c < R) s[bc * lds + r0 + c] = g.s;
     }
   }
   if (t < 128) {
     const GroupQ g = group_setup_bf16(cmx, stab);
+    GroupQ2 g2;
+    if (!group_setup2(g, g2)) *tiny = 1;
     colq[(t & 7) * 16 + (t >> 3)] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
+    colq2[(t & 7) * 16 + (t >> 3)] = make_float4(g2.rhi, g2.rlo, g.s, 0.0f);
     if (FULL || bc * 128 + t < C) sT[br * ldsT + bc * 128 + t] = g.s;
   }
   lds_barrier();
-  GroupQ gc[8];
-  uint32_t cmask[2] = {0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float4 e = colq[j * 16 + c];
-    gc[j].s_n = e.x; gc[j].r_n = e.y; gc[j].k = __float_as_int(e.z); gc[j].s = e.w;
-    if (e.w != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
-  }
   uint32_t rw[8][2];
+  if (*tiny == 0) {
+    GroupQ2 gc[8];
+    uint32_t cmask[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 e = rowq[i * 16 + rb];
-    GroupQ g;
-    g.s_n = e.x; g.r_n = e.y; g.k = __float_as_int(e.z); g.s = e.w;
-    const uint32_t keep = (g.s == 0.0f) ? 0u : 0xffffffffu;
-    const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
-    const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
-    rw[i][0] = cmask[0] & code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
-    rw[i][1] = cmask[1] & code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
-    const int64_t r = r0 + i;
-    if (FULL) {
-      *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
-    } else if (r < R && c0 < C) {
-      store8(q + r * ldq + c0, c0, C, lo, hi);
+    for (int j = 0; j < 8; ++j) {
+      const float4 e = colq2[j * 16 + c];
+      gc[j].rhi = e.x; gc[j].rlo = e.y;
+      if (e.z != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 e = rowq2[i * 16 + rb];
+      GroupQ2 g;
+      g.rhi = e.x; g.rlo = e.y;
+      const uint32_t keep = (e.z == 0.0f) ? 0u : 0xffffffffu;
+      const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
+      const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
+      rw[i][0] = cmask[0] & code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
+      rw[i][1] = cmask[1] & code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
+      const int64_t r = r0 + i;
+      if (FULL) {
+        *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
+      } else if (r < R && c0 < C) {
+        store8(q + r * ldq + c0, c0, C, lo, hi);
+      }
+    }
+  } else {
+    GroupQ gc[8];
+    uint32_t cmask[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 e = colq[j * 16 + c];
+      gc[j].s_n = e.x; gc[j].r_n = e.y; gc[j].k = __float_as_int(e.z); gc[j].s = e.w;
+      if (e.w != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 e = rowq[i * 16 + rb];
+      GroupQ g;
+      g.s_n = e.x; g.r_n = e.y; g.k = __float_as_int(e.z); g.s = e.w;
+      const uint32_t keep = (g.s == 0.0f) ? 0u : 0xffffffffu;
+      const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
+      const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
+      rw[i][0] = cmask[0] & code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
+      rw[i][1] = cmask[1] & code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
+      const int64_t r = r0 + i;
+      if (FULL) {
+        *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
+      } else if (r < R && c0 < C) {
+        store8(q + r * ldq + c0, c0, C, lo, hi);
+      }
     }
   }
   // Token-dimension codes: 4x4 byte transposes into words of 4 tokens each.
@@ -536,8 +624,11 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
   __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
   __shared__ float4 rowq[128], colq[128];   // per-group constants {s_n, r_n, k, s} of the tile
+  __shared__ float4 rowq2[128], colq2[128]; // two-operation constants {rhi, rlo, s, 0}
+  __shared__ int tiny;                       // some group of the tile has no finite reciprocal
   const int t = threadIdx.x;
   if (t < 128) stab[t] = kSetupTab.e[t];
+  if (t == 0) tiny = 0;
   const int64_t br = blockIdx.x / nbc, bc = blockIdx.x % nbc;   // one-dimensional grid, column tiles fastest
   const bool full = (br + 1) * 128 <= R && (bc + 1) * 128 <= C;
   const int c = t & 15, rb = t >> 4;
@@ -569,8 +660,12 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       }
     }
   }
-  if (full) dual_encode<true>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage, rowq, colq);
-  else dual_encode<false>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage, rowq, colq);
+  if (full)
+    dual_encode<true>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage, rowq, colq, rowq2, colq2,
+                      &tiny);
+  else
+    dual_encode<false>(v, br, bc, R, C, q, ldq, s, lds, qT, ldqT, sT, ldsT, cred, stab, stage, rowq, colq, rowq2,
+                       colq2, &tiny);
 }
 
 // RMSNorm statistics: rstd[r] = 1 / sqrt(mean_c x[r, c]^2 + eps) in binary32,

@@ -45,6 +45,47 @@ extern "C" int codec_quotient_scan(uint32_t amax_lo, uint32_t amax_hi, uint64_t*
   return (int)(bad > 0x7fffffff ? 0x7fffffff : bad);
 }
 
+// The two-operation quotient (group_setup2 / group_quotient2, constants from
+// the table-driven setup as in the kernels) against IEEE division, both signs,
+// for every BF16 pair with |x| <= amax whose reciprocal is finite: returns the
+// number of pairs whose E4M3 codes differ.  *n_checked counts the pairs,
+// *n_q_diff those whose binary32 quotients differ (allowed), *n_skipped the
+// maxima whose reciprocal overflows (they keep the normalised quotient).
+extern "C" int codec_quotient2_scan(uint64_t* n_checked, uint64_t* n_q_diff, uint64_t* n_skipped) {
+  static constexpr fp8blk::SetupTable kTab = fp8blk::make_setup_table();
+  long long bad = 0;
+  unsigned long long checked = 0, qdiff = 0, skipped = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(+ : bad, checked, qdiff, skipped)
+  for (uint32_t ab = 1; ab < 0x7f80; ++ab) {
+    const float amax = fp8blk::bf16_to_f32(ab);
+    const fp8blk::GroupQ g = fp8blk::group_setup_bf16(amax, kTab.e);
+    fp8blk::GroupQ2 g2;
+    if (!fp8blk::group_setup2(g, g2)) {
+      ++skipped;
+      continue;
+    }
+    for (uint32_t xb = 0; xb <= ab; ++xb) {
+      for (uint32_t sgn = 0; sgn < 2; ++sgn) {
+        const float x = fp8blk::bf16_to_f32(xb | (sgn << 15));
+        const float q2 = fp8blk::group_quotient2(x, g2);
+        const float qr = x / g.s;
+        ++checked;
+        qdiff += fp8blk::f32_bits(q2) != fp8blk::f32_bits(qr);
+        const uint32_t c2 = fp8blk::e4m3_encode(q2), cr = fp8blk::e4m3_encode(qr);
+        if (c2 != cr) {
+          if (bad < 10) std::printf("QUOTIENT2 MISMATCH amax=%#x x=%#x q2=%a ref=%a codes %#x %#x\n", ab,
+                                    xb | (sgn << 15), q2, qr, c2, cr);
+          ++bad;
+        }
+      }
+    }
+  }
+  if (n_checked) *n_checked = checked;
+  if (n_q_diff) *n_q_diff = qdiff;
+  if (n_skipped) *n_skipped = skipped;
+  return (int)(bad > 0x7fffffff ? 0x7fffffff : bad);
+}
+
 // Table-driven group setup against group_setup for every BF16 magnitude:
 // returns the number of maxima whose four constants differ in any bit.  The
 // table is the compile-time one the kernels copy; its entries must also equal

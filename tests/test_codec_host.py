@@ -8,6 +8,11 @@
    binary32 in [2^-12, 2^10) and on a random sample of all bit patterns.
 3. The table-driven group setup the kernels use for BF16 group maxima gives
    the same four constants as the direct one for every BF16 magnitude.
+4. The two-operation quotient (reciprocal rounded down plus its exact
+   residual term) gives the same E4M3 code as IEEE division for every pair
+   of BF16 values with |x| <= amax, both signs, wherever its reciprocal is
+   finite; the maxima where it is not are all below 1.4e-36 and keep the
+   normalised quotient.
 """
 
 import ctypes
@@ -38,6 +43,8 @@ def codec_lib(tmp_path_factory):
     lib.codec_quotient_scan.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint64)]
     lib.codec_quotient_scan.restype = ctypes.c_int
     lib.codec_setup_table_scan.restype = ctypes.c_int
+    lib.codec_quotient2_scan.argtypes = [ctypes.POINTER(ctypes.c_uint64)] * 3
+    lib.codec_quotient2_scan.restype = ctypes.c_int
     return lib
 
 
@@ -50,6 +57,19 @@ def test_exact_quotient_equals_ieee_division_for_all_bf16_pairs(codec_lib):
     bad = codec_lib.codec_quotient_scan(1, 0x7F80, ctypes.byref(n))
     assert n.value > 1_000_000_000
     assert bad == 0
+
+
+def test_two_operation_quotient_gives_the_ieee_codes_for_all_bf16_pairs(codec_lib):
+    n, qdiff, skipped = ctypes.c_uint64(0), ctypes.c_uint64(0), ctypes.c_uint64(0)
+    bad = codec_lib.codec_quotient2_scan(ctypes.byref(n), ctypes.byref(qdiff), ctypes.byref(skipped))
+    assert bad == 0
+    assert n.value > 1_000_000_000
+    # The maxima without a finite reciprocal: every BF16 magnitude below
+    # 0x03E1 (about 1.32e-36) and nothing above it.
+    assert skipped.value == 0x03E1 - 1
+    # The binary32 quotients differ in some pairs (so the check is not vacuous),
+    # never their codes.
+    assert qdiff.value > 0
 
 
 def _encode(lib, v):

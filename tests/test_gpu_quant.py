@@ -146,6 +146,24 @@ def test_special_values(B):
     assert 0 < s[0, 3] < np.finfo(np.float32).tiny
 
 
+def test_maxima_without_finite_reciprocal(B):
+    """Groups whose maximum is below about 1.3e-36 have no finite binary32
+    reciprocal of their scale; a wave or tile holding one takes the normalised
+    quotient instead of the two-operation one.  Block (0, 0) holds only such
+    values (so do the token groups of its columns and the row groups of its
+    rows), the rest of the tensor is ordinary, so both forms meet in one call."""
+    rng = np.random.default_rng(17)
+    x = W.normal_bf16((256, 384), 1.0, W.seed_for(92, 0, 0, "x"))
+    tiny = rng.integers(1, 0x03E1, size=(128, 128)).astype(np.uint16)
+    tiny |= (rng.integers(0, 2, size=(128, 128)).astype(np.uint16) << 15)
+    x[:128, :128] = tiny
+    x[5, 7] = 0x03E0                          # the largest magnitude of that range
+    check_rows(B, x, "tiny maxima")
+    check_tokens(B, x, "tiny maxima")
+    check_dual(B, x, "tiny maxima")
+    check_blocks(B, x, "tiny maxima")
+
+
 def test_every_bf16_magnitude_as_amax(B):
     bits = np.arange(1, 0x7F80, dtype=np.uint16)
     x = np.zeros((bits.size, 128), dtype=np.uint16)
