@@ -146,7 +146,8 @@ FP8BLK_HD float group_quotient(float x, const GroupQ& g) {
 // signs (checked exhaustively on the host, with the constants formed exactly
 // as here from the table-driven setup); the binary32 quotient itself may
 // differ in its last place where the code cannot.  Zero groups get
-// rhi = rlo = 0 (their codes are forced to 0x00 by the caller).
+// rhi = -0 and rlo = +0: their elements are +-0, and x * (-0) + x * (+0) is
+// +0 for both signs of zero, so their codes come out 0x00 with no mask.
 struct GroupQ2 {
   float rhi;
   float rlo;
@@ -155,7 +156,7 @@ struct GroupQ2 {
 // The two-operation constants of group g; false if 1 / s overflows binary32,
 // in which case the caller must use group_quotient.
 FP8BLK_HD bool group_setup2(const GroupQ& g, GroupQ2& o) {
-  o.rhi = 0.0f;
+  o.rhi = -0.0f;
   o.rlo = 0.0f;
   if (g.s == 0.0f) return true;
   // fl32(1 / s) = 2^k * fl32(1 / s_n) exactly: the scaling is by a power of

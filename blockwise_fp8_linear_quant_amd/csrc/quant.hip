@@ -189,9 +189,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const bool fast = wave_all(group_setup2(gq, g2));
   const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;   // zero group -> codes 0x00
   uint32_t w[4];
-  if (fast) {
+  if (fast) {   // zero groups come out 0x00 by themselves (group_setup2)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) w[d] = keep & code4(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], g2);
+    for (int d = 0; d < 4; ++d) w[d] = code4(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], g2);
   } else {
 #pragma unroll
     for (int d = 0; d < 4; ++d) w[d] = keep & code4(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], gq);
@@ -255,14 +255,13 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   const bool fast = wave_all(ok);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint32_t keep = (sc[j] == 0.0f) ? 0u : 0xffffffffu;
     uint32_t w[4];
-    if (fast) {
+    if (fast) {   // zero groups come out 0x00 by themselves (group_setup2)
 #pragma unroll
       for (int d = 0; d < 4; ++d)
-        w[d] = keep & code4(elem(v[4 * d], j), elem(v[4 * d + 1], j), elem(v[4 * d + 2], j), elem(v[4 * d + 3], j),
-                            g2[j]);
+        w[d] = code4(elem(v[4 * d], j), elem(v[4 * d + 1], j), elem(v[4 * d + 2], j), elem(v[4 * d + 3], j), g2[j]);
     } else {
+      const uint32_t keep = (sc[j] == 0.0f) ? 0u : 0xffffffffu;
       const GroupQ gq = group_setup(am[j]);
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -318,13 +317,13 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
   const uint32_t keep = (gq.s == 0.0f) ? 0u : 0xffffffffu;
   // Row-major codes: rw[i][0] = columns 0..3 of row i, rw[i][1] = columns 4..7.
   uint32_t rw[8][2];
-  if (fast) {
+  if (fast) {   // a zero block comes out 0x00 by itself (group_setup2)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        rw[i][hh] = keep & code4(elem(v[i], 4 * hh), elem(v[i], 4 * hh + 1), elem(v[i], 4 * hh + 2),
-                                 elem(v[i], 4 * hh + 3), g2);
+        rw[i][hh] = code4(elem(v[i], 4 * hh), elem(v[i], 4 * hh + 1), elem(v[i], 4 * hh + 2), elem(v[i], 4 * hh + 3),
+                          g2);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -472,7 +471,7 @@ __device__ __forceinline__ void dual_encode(
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
     float (*cred)[128], const SetupEntry* stab, uint4* stage, float4* rowq, float4* colq,
-    float4* rowq2, float4* colq2, int* tiny) {
+    float2* rowq2, float2* colq2, int* tiny) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t & 15, rb = t >> 4;
   const int64_t r0 = br * 128 + rb * 8, c0 = bc * 128 + c * 8;
@@ -514,7 +513,7 @@ __device__ __forceinline__ void dual_encode(
   // stores its scale, thread t < 128 does the same for column t.  The tables
   // are index-major (rowq[i][rb], colq[j][c]): the 16 lanes of a read either
   // share one row entry or take 16 consecutive column entries, free of bank
-  // conflicts.  rowq2/colq2 hold the two-operation constants {rhi, rlo, s};
+  // conflicts.  rowq2/colq2 hold the two-operation constants {rhi, rlo};
   // a group whose reciprocal overflows sets *tiny, and the whole tile then
   // takes the normalised quotient from rowq/colq {s_n, r_n, k, s}.
   {
@@ -526,7 +525,7 @@ __device__ __forceinline__ void dual_encode(
       GroupQ2 g2;
       if (!group_setup2(g, g2)) *tiny = 1;
       rowq[c * 16 + rb] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
-      rowq2[c * 16 + rb] = make_float4(g2.rhi, g2.rlo, g.s, 0.0f);
+      rowq2[c * 16 + rb] = make_float2(g2.rhi, g2.rlo);
       if (FULL || r0 + c < R) s[bc * lds + r0 + c] = g.s;
     }
   }
@@ -535,30 +534,28 @@ __device__ __forceinline__ void dual_encode(
     GroupQ2 g2;
     if (!group_setup2(g, g2)) *tiny = 1;
     colq[(t & 7) * 16 + (t >> 3)] = make_float4(g.s_n, g.r_n, __int_as_float(g.k), g.s);
-    colq2[(t & 7) * 16 + (t >> 3)] = make_float4(g2.rhi, g2.rlo, g.s, 0.0f);
+    colq2[(t & 7) * 16 + (t >> 3)] = make_float2(g2.rhi, g2.rlo);
     if (FULL || bc * 128 + t < C) sT[br * ldsT + bc * 128 + t] = g.s;
   }
   lds_barrier();
   uint32_t rw[8][2];
   if (*tiny == 0) {
+    // Zero groups come out 0x00 by themselves here (group_setup2).
     GroupQ2 gc[8];
-    uint32_t cmask[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float4 e = colq2[j * 16 + c];
+      const float2 e = colq2[j * 16 + c];
       gc[j].rhi = e.x; gc[j].rlo = e.y;
-      if (e.z != 0.0f) cmask[j >> 2] |= 0xffu << (8 * (j & 3));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float4 e = rowq2[i * 16 + rb];
+      const float2 e = rowq2[i * 16 + rb];
       GroupQ2 g;
       g.rhi = e.x; g.rlo = e.y;
-      const uint32_t keep = (e.z == 0.0f) ? 0u : 0xffffffffu;
-      const uint32_t lo = keep & code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
-      const uint32_t hi = keep & code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
-      rw[i][0] = cmask[0] & code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
-      rw[i][1] = cmask[1] & code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
+      const uint32_t lo = code4(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), g);
+      const uint32_t hi = code4(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), g);
+      rw[i][0] = code4_each(elem(v[i], 0), elem(v[i], 1), elem(v[i], 2), elem(v[i], 3), gc, 0);
+      rw[i][1] = code4_each(elem(v[i], 4), elem(v[i], 5), elem(v[i], 6), elem(v[i], 7), gc, 4);
       const int64_t r = r0 + i;
       if (FULL) {
         *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
@@ -624,7 +621,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   __shared__ SetupEntry stab[128];   // group constants by BF16 significand (see group_setup_bf16)
   __shared__ uint4 stage[1024];      // transposed code tile (store_codes_transposed)
   __shared__ float4 rowq[128], colq[128];   // per-group constants {s_n, r_n, k, s} of the tile
-  __shared__ float4 rowq2[128], colq2[128]; // two-operation constants {rhi, rlo, s, 0}
+  __shared__ float2 rowq2[128], colq2[128]; // two-operation constants {rhi, rlo}
   __shared__ int tiny;                       // some group of the tile has no finite reciprocal
   const int t = threadIdx.x;
   if (t < 128) stab[t] = kSetupTab.e[t];

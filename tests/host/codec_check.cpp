@@ -80,6 +80,20 @@ extern "C" int codec_quotient2_scan(uint64_t* n_checked, uint64_t* n_q_diff, uin
       }
     }
   }
+  // A zero group (amax = 0): both signed zeros must give code 0x00 (no mask).
+  {
+    const fp8blk::GroupQ g = fp8blk::group_setup(0.0f);
+    fp8blk::GroupQ2 g2;
+    const bool ok2 = fp8blk::group_setup2(g, g2);
+    const uint32_t zeros[2] = {0x0000u, 0x8000u};
+    for (uint32_t xb : zeros) {
+      const uint32_t code = fp8blk::e4m3_encode(fp8blk::group_quotient2(fp8blk::bf16_to_f32(xb), g2));
+      if (!ok2 || code != 0u) {
+        std::printf("ZERO GROUP x=%#x code %#x\n", xb, code);
+        ++bad;
+      }
+    }
+  }
   if (n_checked) *n_checked = checked;
   if (n_q_diff) *n_q_diff = qdiff;
   if (n_skipped) *n_skipped = skipped;
