@@ -622,6 +622,224 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   }
 }
 
+// Exact path, 128 x 128 tiles of 8 waves in two K groups.  Waves 0-3 and 4-7
+// each cover the tile with 64 x 64 sub-tiles and contract one half of the
+// scale blocks (the first and the second half) through double-buffered
+// stages of their own; the second group's accumulators are then added to the
+// first group's through LDS, one FP32 add per element in that fixed order, and
+// the first group stores the tile.  For grids of about one 128 x 128 tile per
+// CU this gives every SIMD two waves instead of one.  Both groups meet every
+// workgroup barrier, so the number of scale blocks must be even.
+template <int SB_MODE, int OUT>
+__global__ __launch_bounds__(512, 1) void block_gemm_f16_kgroups_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA, int64_t ldsa,
+    const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ SB, int64_t ldsb,
+    int64_t I, int64_t L, void* __restrict__ Cout, int64_t ldc, int tilesM, int tilesN) {
+  constexpr int BM = 128, BN = 128, WM = 64, WN = 64, NWG = 4, NS = 2;
+  using C = Cfg<BM, BN, WM, WN, SB_MODE, PREC_F16, NWG, NS>;
+  constexpr int MT = C::MT, NT = C::NT;
+  // Stage buffers of group 0 and of group 1 (distinct LDS objects).
+  __shared__ __attribute__((aligned(1024))) uint8_t g0s0[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t g0s1[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t g1s0[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t g1s1[C::kBufBytes];
+  __shared__ __attribute__((aligned(16))) float sb_ring[2][SB_MODE == SB_ROWS ? C::kRing * BN : 4];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int grp = wave >> 2, lw = wave & 3;
+  int tm, tn, split;
+  map_tile<group_rows<BM>(), 1>(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn, split);
+  const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+  const int wm = lw / C::WGN, wn = lw % C::WGN;
+  const int nLBtot = (int)(L / BK);
+  const int nLB = nLBtot / 2;            // this group's scale blocks
+  const int lb0 = grp * nLB;
+  const int h = lane >> 5, rr = lane & 31;
+  uint8_t* const lds0 = grp ? g1s0 : g0s0;
+  uint8_t* const lds1 = grp ? g1s1 : g0s1;
+  float* const ring = sb_ring[grp];
+
+  float acc[MT][NT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
+
+  TileStager<BM, NWG> sta;
+  TileStager<BN, NWG> stb;
+  ScaleStager<BM, NWG> ssa;
+  ScaleStager<BN, NWG> ssb;
+  sta.init(lda, i0, I - 1, lw, lane);
+  stb.init(ldb, j0, j0 + BN - 1, lw, lane);
+  ssa.init(i0, I - 1, lw, lane);
+  ssb.init(j0, j0 + BN - 1, lw, lane);
+  auto stage_all = [&](int lbl, uint8_t* buf) {
+    const int64_t lb = lb0 + lbl;
+    sta.issue(A + i0 * lda + lb * BK, buf, lw);
+    stb.issue(B + j0 * ldb + lb * BK, buf + BM * BK, lw);
+    ssa.issue(SA + lb * ldsa + i0, reinterpret_cast<float*>(buf + C::kSaOff), lw, lane);
+    if (SB_MODE == SB_ROWS) ssb.issue(SB + lb * ldsb + j0, ring + (lbl % C::kRing) * BN, lw, lane);
+  };
+
+  uint4 qa[2][MT], qb[2][NT];   // raw codes of two K slices (software pipeline)
+  v8h fa[MT][2], fb[NT][2];     // converted operands of the slice being multiplied
+  v16f p[MT][NT];               // block products
+  auto load_slice = [&](const uint8_t* buf, int c, int slot) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) qa[slot][mt] = lds16(buf, wm * WM + mt * 32 + rr, 4 * h + c);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) qb[slot][nt] = lds16(buf + BM * BK, wn * WN + nt * 32 + rr, 4 * h + c);
+    __builtin_amdgcn_sched_barrier(0x0006);
+  };
+  auto convert = [&](int slot) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      fa[mt][0] = cvt8(qa[slot][mt].x, qa[slot][mt].y);
+      fa[mt][1] = cvt8(qa[slot][mt].z, qa[slot][mt].w);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      fb[nt][0] = cvt8(qb[slot][nt].x, qb[slot][nt].y);
+      fb[nt][1] = cvt8(qb[slot][nt].z, qb[slot][nt].w);
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          p[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[nt][k], fa[mt][k], p[mt][nt], 0, 0, 0);
+  };
+
+  // Block lb of this group from `cur` (its slice 0 already in registers), as
+  // in block_gemm_f16_kernel with double buffering: slices 1..3 read one ahead
+  // of the multiply; after the block-end barrier `cur` is refilled with block
+  // lb + 2 and slice 0 of block lb + 1 is read from `nxt` while the last slice
+  // is multiplied.
+  auto step = [&](uint8_t* cur, const uint8_t* nxt, int lb) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) p[mt][nt] = v16f{};
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      load_slice(cur, c + 1, (c + 1) & 1);
+      convert(c & 1);
+      multiply();
+    }
+    convert(1);
+    const float* lsa = reinterpret_cast<const float*>(cur + C::kSaOff);
+    float sa[MT];                  // A scale of this lane's output row
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sa[mt] = lsa[wm * WM + mt * 32 + rr];
+    const float sblk = (SB_MODE == SB_BLOCK) ? SB[(j0 / 128) * nLBtot + lb0 + lb] : 1.0f;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    if (lb + NS < nLB) stage_all(lb + NS, cur);
+    if (lb + 1 < nLB) load_slice(nxt, 0, 0);
+    multiply();
+    float4 sbr[NT][4];             // SB_ROWS: B scales of output columns 8q + 4h + u
+    const float* lsb = ring + (lb % C::kRing) * BN;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sbr[nt][q] = (SB_MODE == SB_ROWS) ? *reinterpret_cast<const float4*>(lsb + wn * WN + nt * 32 + 8 * q + 4 * h)
+                                          : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float srow = (SB_MODE == SB_BLOCK) ? sa[mt] * sblk : sa[mt];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float cs[4] = {sbr[nt][q].x, sbr[nt][q].y, sbr[nt][q].z, sbr[nt][q].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float sc = (SB_MODE == SB_ROWS) ? srow * cs[u] : srow;
+            acc[mt][nt][4 * q + u] = fmaf(p[mt][nt][4 * q + u], sc, acc[mt][nt][4 * q + u]);
+          }
+        }
+    }
+  };
+
+  // Prologue: both stages of this group, wait for its first block.
+  stage_all(0, lds0);
+  if (nLB > 1) stage_all(1, lds1);
+  if (nLB > 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kVmemPerBlock));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  load_slice(lds0, 0, 0);
+  for (int lb = 0; lb < nLB; lb += 2) {
+    step(lds0, lds1, lb);
+    if (lb + 1 < nLB) step(lds1, lds0, lb + 1);
+  }
+
+  // The second group's accumulators, lane-major (one 1 KB run per wave store),
+  // through its own stage buffers: sub-tile row mt = 0 into the first, 1 into
+  // the second.  Then the first group adds them (its own value first) and
+  // stores the tile; the second group is done.
+  lds_barrier();
+  if (grp == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float* dst = reinterpret_cast<float*>(mt == 0 ? g1s0 : g1s1) + (lw * NT * 4) * 256 + lane * 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(dst + (nt * 4 + q) * 256) =
+              make_float4(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
+    }
+  }
+  lds_barrier();
+  if (grp == 1) return;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float* src = reinterpret_cast<const float*>(mt == 0 ? g1s0 : g1s1) + (lw * NT * 4) * 256 + lane * 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 o = *reinterpret_cast<const float4*>(src + (nt * 4 + q) * 256);
+        acc[mt][nt][4 * q] += o.x;
+        acc[mt][nt][4 * q + 1] += o.y;
+        acc[mt][nt][4 * q + 2] += o.z;
+        acc[mt][nt][4 * q + 3] += o.w;
+      }
+  }
+
+  // Epilogue of the first group, one 32-row band at a time through its own
+  // stage buffers (no other wave uses them any more).
+  {
+    using Bd = Band<OUT, WN>;
+    uint8_t* region = band_region<32 * Bd::RS, C::kBufBytes, NS, NWG>(g0s0, g0s1, g0s1, lw);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float* v = &acc[mt][nt][4 * q];
+          uint8_t* pp = region + rr * Bd::RS + (nt * 32 + 8 * q + 4 * h) * Bd::ESZ;
+          if (OUT == OUT_BF16) {
+            *reinterpret_cast<uint2*>(pp) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
+          } else {
+            *reinterpret_cast<float4*>(pp) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      store_band<OUT, WN, 32>(region, lane, Cout, ldc, i0 + wm * WM + mt * 32, j0 + wn * WN, I);
+    }
+  }
+}
+
 // FP8 matrix-core path: one workgroup per output tile, the exact path's
 // pipeline with the block product formed by v_mfma_f32_32x32x64_f8f6f4 on the
 // E4M3 codes themselves (two per 32x32 sub-tile and block, no conversion).
@@ -1056,9 +1274,10 @@ void launch_planes(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
 // FP8BLK_GEMM_SPLIT2) or on 128 x 128 tiles into partial planes (split 2, 4 or
 // 8 ways, the default for small grids); otherwise 256 x 128 output tiles (8 waves of 64 x 64,
 // triple-buffered LDS, one workgroup per CU) when they fill every CU for a
-// whole number of rounds, else 128 x 128 tiles (4 waves, double-buffered, two
-// workgroups per CU), whose finer granularity keeps every CU busy in a partial
-// last round.
+// whole number of rounds, else 128 x 128 tiles: on the exact path with at
+// most one tile per CU, 8 waves in two K groups (block_gemm_f16_kgroups_kernel),
+// otherwise 4 waves, double-buffered, two workgroups per CU, whose finer
+// granularity keeps every CU busy in a partial last round.
 template <int SB_MODE, int OUT, int PREC>
 void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
                  const uint8_t* B, int64_t ldb, const float* SB, int64_t ldsb,
@@ -1071,6 +1290,11 @@ void launch_prec(const uint8_t* A, int64_t lda, const float* SA, int64_t ldsa,
   else if (plan.big_tiles)
     launch_cfg<256, 128, 64, 64, SB_MODE, OUT, PREC, 8, 3, 1>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc,
                                                               nullptr, nullptr, st);
+  else if (PREC == PREC_F16 && plan.kgroups) {
+    const int tilesM = (int)((I + 127) / 128), tilesN = (int)(J / 128);
+    hipLaunchKernelGGL((block_gemm_f16_kgroups_kernel<SB_MODE, OUT>), dim3(tilesM * tilesN), dim3(512), 0, st,
+                       A, lda, SA, ldsa, B, ldb, SB, ldsb, I, L, C, ldc, tilesM, tilesN);
+  }
   else
     launch_cfg<128, 128, 64, 64, SB_MODE, OUT, PREC, 4, 2, 1>(A, lda, SA, ldsa, B, ldb, SB, ldsb, I, J, L, C, ldc,
                                                               nullptr, nullptr, st);
@@ -1146,6 +1370,13 @@ SplitPlan plan_split(int64_t I, int64_t J, int64_t L, void* ws, size_t ws_bytes,
   SplitPlan p;
   const int64_t big = ((I + 255) / 256) * (J / 128);
   p.big_tiles = big >= kCUs && big % kCUs == 0;
+  // At most one 128 x 128 tile per CU (a 2048 x 2048 weight gradient: 256
+  // tiles): two K groups of 4 waves per tile, so that every SIMD runs two
+  // waves (measured on the O weight gradient over 4096 tokens: 48 -> 43 us).
+  // Grids with more tiles already run two 4-wave workgroups per CU, where
+  // 8-wave tiles were slower (the down projection's: 114 -> 123 us).
+  const int64_t tiles128 = ((I + 127) / 128) * (J / 128);
+  p.kgroups = !p.big_tiles && tiles128 <= kCUs && (L / 128) % 2 == 0;
   if (force) {
     const size_t need = split_workspace_bytes(I, J, 2);
     if (L / 128 >= 2 && need > 0 && ws != nullptr && ws_bytes >= need) {
@@ -1158,6 +1389,7 @@ SplitPlan plan_split(int64_t I, int64_t J, int64_t L, void* ws, size_t ws_bytes,
     if (s > 1 && need > 0 && ws != nullptr && ws_bytes >= need) p.splits = s;
   }
   if (p.splits > 1) {
+    p.kgroups = false;
     p.counters = p.split_big_tiles ? static_cast<unsigned*>(ws) : nullptr;
     p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
   }

@@ -39,6 +39,7 @@ struct SplitPlan {
   bool big_tiles = false;        // unsplit: 256 x 128 tiles (else 128 x 128)
   int splits = 1;
   bool split_big_tiles = false;  // split: 256 x 128 tiles (else 128 x 128)
+  bool kgroups = false;          // unsplit 128 x 128 exact path: 8 waves in two K groups (at most one tile per CU)
   unsigned* counters = nullptr;
   float* part = nullptr;
 };
@@ -51,7 +52,8 @@ int small_grid_splits(int64_t I, int64_t J, int64_t L);
 size_t small_split_workspace_bytes(int64_t I, int64_t J, int splits);
 // The plan for a call: with `force`, split in two on 256 x 128 tiles when the
 // workspace holds split_workspace_bytes(I, J, 2); otherwise the default split
-// when the workspace holds its bytes; else one split.
+// when the workspace holds its bytes; else one split (with `kgroups` for
+// grids of at most one 128 x 128 tile per CU and an even number of blocks).
 SplitPlan plan_split(int64_t I, int64_t J, int64_t L, void* ws, size_t ws_bytes, bool force);
 
 // C[I, J] = sum_lb SA(i, lb) SB(j, lb) sum_{l in lb} A[i, l] B[j, l]

@@ -267,6 +267,49 @@ def test_empty_contraction_and_empty_outputs(B):
     assert y.shape == (0, 128)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 384, 512), (1000, 1024, 256)])
+def test_two_k_groups_unsplit(B, M, N, K):
+    """Without a workspace, a grid of at most one 128 x 128 tile per CU whose
+    contraction has an even number of 128-blocks runs as two K groups of four
+    waves, each over half the blocks, summed before the epilogue.  (1000, 1024,
+    256) takes that kernel in all three GEMMs; (300, 384, 512) in the forward
+    only (odd block counts elsewhere take the 4-wave tiles).  Every element of
+    the BF16 forward, the FP32 dgrad and the wgrad (overwrite and accumulate)."""
+    torch = _torch()
+    xb = W.normal_bf16((M, K), 1.0, W.seed_for(97, M, 0, "x"))
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(97, M, 0, "w"))
+    dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(97, M, 0, "dy"))
+    x, w, dy = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+    xq, sx = B.fp8_quant_1x128(x)
+    wq, sw, wqT, swT = B.fp8_quant_128x128(w, with_transpose=True)
+    dyq, sdy = B.fp8_quant_1x128(dy)
+    dyqT, sdyT = B.fp8_quant_1x128(dy, transpose_out=True)
+    xqT, sxT = B.fp8_quant_1x128(x, transpose_out=True)
+    oxq, osx = quant.quant_1x128_rows(xb)
+    owq, osw = quant.quant_128x128(wb)
+    owqT, oswT = quant.quant_128x128(np.ascontiguousarray(wb.T))
+    odyq, osdy = quant.quant_1x128_rows(dyb)
+    odyqT, osdyT = quant.quant_1x128_tokens(dyb)
+    oxqT, osxT = quant.quant_1x128_tokens(xb)
+    say("gemm two K groups fwd", (M, N, K))
+    y = B.fp8_block_gemm_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16, workspace=False)
+    check_full(host(y), lambda: gemm.fwd(oxq, osx, owq, osw), "bf16", f"fwd {M}x{N}x{K}")
+    say("gemm two K groups dgrad", (M, N, K))
+    dx = B.fp8_block_gemm_dgrad(dyq, sdy, wqT, swT, out_dtype=torch.float32, workspace=False)
+    check_full(host(dx), lambda: gemm.dgrad(odyq, osdy, owqT, oswT), "f32", f"dgrad {M}x{N}x{K}")
+    say("gemm two K groups wgrad", (M, N, K))
+    ref = lambda: gemm.wgrad(odyqT, osdyT, oxqT, osxT)
+    dw = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, workspace=False)
+    check_full(host(dw), ref, "f32", f"wgrad {M}x{N}x{K}")
+    dw0 = np.random.default_rng(M + 7).standard_normal((N, K)).astype(np.float32) * 1e-3
+    dwa = B.fp8_block_gemm_wgrad(dyqT, sdyT, xqT, sxT, M=M, dw=torch.from_numpy(dw0).cuda(), accumulate=True,
+                                 workspace=False)
+    yv, bnd = ref()
+    ok, rep = compare.check_fp32(host(dwa), yv + dw0.astype(np.float64),
+                                 bnd + np.abs(dw0) * (2.0 ** -23 / compare.FP32_RTOL))
+    assert ok, f"wgrad accumulate {M}x{N}x{K}: {rep}"
+
+
 def test_determinism(B):
     torch = _torch()
     xb = W.normal_bf16((512, 1024), 1.0, 8)
