@@ -742,7 +742,8 @@ def main():
                      "frac_of_issued_f16_peak": round(gemm_tflops / PEAK_TFLOPS["f16"], 4),
                      "traffic": round(traffic) if traffic is not None else None,
                      "algorithmic_bytes_per_launch": round(alg_bytes),
-                     "kernel": "block_gemm_f16_kernel (E4M3 codes -> exact F16 MFMA, FP32 block rescale)",
+                     "kernel": "block_gemm_f16_kernel / block_gemm_f16_kgroups_kernel (E4M3 codes -> exact F16 MFMA, "
+                               "FP32 block rescale)",
                      "launches_per_step": n_launch,
                      "avg_launch_us": round(gemm_ms / n_launch * 1e3, 2),
                      "gemm_ms_per_step": round(gemm_ms, 4),

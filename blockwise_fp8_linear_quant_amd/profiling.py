@@ -35,9 +35,15 @@ import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/fp8_codec.h", "build.py")
-GEMM_KERNEL = "block_gemm_f16_kernel"
+# The exact path's GEMM kernels: 256 x 128 and 128 x 128 tiles, and 128 x 128
+# tiles of eight waves in two contraction groups.
+GEMM_KERNELS = ("block_gemm_f16_kernel", "block_gemm_f16_kgroups_kernel")
 FP8_KERNEL = "block_gemm_fp8_kernel"
 COPY_KERNEL_HINTS = ("copy", "elementwise")
+
+
+def is_exact_gemm(name):
+    return any(k in name for k in GEMM_KERNELS)
 
 
 def source_digest(files=GEMM_SOURCES):
@@ -77,13 +83,14 @@ def stats_summary(stats_csv, command, bench_json=None):
     bench = json.loads(open(bench_json).read().strip().splitlines()[-1]) if bench_json else {}
     # Each GEMM kernel family beside bench.py's own figure from the same
     # profiled process (HIP events around the timed steps on the GEMMs' stream).
-    for kernel, key, rate in ((GEMM_KERNEL, "roofline", "achieved"), (FP8_KERNEL, "fp8_matrix_core_path", "gemm_tflops")):
-        sel = [r for r in rows if kernel in r["Name"]]
+    for kernels, key, rate in ((GEMM_KERNELS, "roofline", "achieved"),
+                               ((FP8_KERNEL,), "fp8_matrix_core_path", "gemm_tflops")):
+        sel = [r for r in rows if any(k in r["Name"] for k in kernels)]
         if not sel:
             continue
         calls = sum(int(r["Calls"]) for r in sel)
         avg_us = sum(float(r["TotalDurationNs"]) for r in sel) / calls / 1e3
-        lines += ["", f"{kernel} (all instantiations): {calls} calls, average {avg_us:.2f} us"]
+        lines += ["", f"{' + '.join(kernels)} (all instantiations): {calls} calls, average {avg_us:.2f} us"]
         rec = bench.get(key)
         if rec and "avg_launch_us" in rec:
             lines += [f"bench.py in the same run: average launch {rec['avg_launch_us']:.2f} us over "
@@ -113,7 +120,7 @@ def traffic_summary(fetch_csv, write_csv, copy_bytes, command, algorithmic_bytes
 
     def copy_value(tab):
         cands = [(d, v) for d, (n, v) in tab.items()
-                 if GEMM_KERNEL not in n and any(h in n.lower() for h in COPY_KERNEL_HINTS)]
+                 if not is_exact_gemm(n) and any(h in n.lower() for h in COPY_KERNEL_HINTS)]
         if not cands:
             raise SystemExit("no copy kernel dispatch found in the counter CSV")
         return max(cands, key=lambda dv: dv[1])[1]   # the big copy of known size
@@ -121,8 +128,8 @@ def traffic_summary(fetch_csv, write_csv, copy_bytes, command, algorithmic_bytes
     f_copy_kib, w_copy_kib = copy_value(fetch), copy_value(write)
     f_scale = copy_bytes / f_copy_kib   # bytes per counter unit
     w_scale = copy_bytes / w_copy_kib
-    gf = [v for n, v in fetch.values() if GEMM_KERNEL in n]
-    gw = [v for n, v in write.values() if GEMM_KERNEL in n]
+    gf = [v for n, v in fetch.values() if is_exact_gemm(n)]
+    gw = [v for n, v in write.values() if is_exact_gemm(n)]
     if not gf or not gw:
         raise SystemExit("no block GEMM dispatch in the counter CSVs")
     fetch_b = sum(gf) / len(gf) * f_scale

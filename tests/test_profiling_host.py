@@ -6,6 +6,8 @@ from blockwise_fp8_linear_quant_amd import profiling
 
 GEMM = ("void fp8blk::(anonymous namespace)::block_gemm_f16_kernel<256, 128, 64, 64, 0, 1, 8, 3>"
         "(unsigned char const*, long, float const*, long)")
+KGROUPS = ("void fp8blk::(anonymous namespace)::block_gemm_f16_kgroups_kernel<1, 2>"
+           "(unsigned char const*, long, float const*, long)")
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>(int, float*)"
 
 
@@ -27,14 +29,16 @@ def test_traffic_scales_by_the_copy_probe(tmp_path):
     copy_bytes = 1 << 30
     # counters read half the true bytes for the copy, so the scale is 2048 B per unit
     fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
-    _counters(fetch, "FETCH_SIZE", [(1, COPY, 524288.0), (2, GEMM, 1000.0), (3, GEMM, 3000.0)])
-    _counters(write, "WRITE_SIZE", [(1, COPY, 1048576.0), (2, GEMM, 10.0), (3, GEMM, 30.0)])
+    # both exact-path kernels count as GEMM launches
+    _counters(fetch, "FETCH_SIZE", [(1, COPY, 524288.0), (2, GEMM, 1000.0), (3, KGROUPS, 3000.0)])
+    _counters(write, "WRITE_SIZE", [(1, COPY, 1048576.0), (2, GEMM, 10.0), (3, KGROUPS, 30.0)])
     text = profiling.traffic_summary(str(fetch), str(write), copy_bytes, "cmd", 4096.0 * 1000)
     kv = dict(line.split(": ", 1) for line in text.strip().splitlines())
     assert float(kv["fetch_scale_bytes_per_kib"]) == 2048.0
     assert float(kv["write_scale_bytes_per_kib"]) == 1024.0
     assert int(kv["gemm_fetch_bytes_per_launch"]) == 2000 * 2048
     assert int(kv["gemm_write_bytes_per_launch"]) == 20 * 1024
+    assert int(kv["gemm_dispatches"]) == 2
     assert kv["source_sha256"] == profiling.source_digest()
 
 
@@ -52,7 +56,8 @@ def test_stats_summary_sets_rocprof_beside_the_bench_figure(tmp_path):
     with open(stats, "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"])
-        w.writerow([GEMM, 12, 1200000, 100000, 80.0])
+        w.writerow([GEMM, 11, 1150000, 104545, 76.0])
+        w.writerow([KGROUPS, 1, 50000, 50000, 4.0])
         w.writerow([COPY, 4, 300000, 75000, 20.0])
     bench = tmp_path / "b.json"
     bench.write_text('noise\n{"roofline": {"avg_launch_us": 125.0, "launches_per_step": 12, "achieved": 900.0}}\n')
