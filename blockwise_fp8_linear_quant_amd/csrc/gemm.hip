@@ -449,7 +449,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
   };
 
   uint4 qa[2][MT], qb[2][NT];   // raw codes of two K slices (software pipeline)
-  v8h fa[MT][2], fb[NT][2];     // converted operands of the slice being multiplied
+  // Converted operands: two K slices with the deeper schedule below, else one.
+  constexpr bool kAhead = NW == 8 && SB_MODE == SB_BLOCK;
+  v8h fa[2][MT][2], fb[2][NT][2];
   v16f p[MT][NT];               // block products
   auto load_slice = [&](const uint8_t* buf, int c, int slot) {
 #pragma unroll
@@ -460,54 +462,76 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     // stay a slice ahead instead of sinking next to their first use.
     __builtin_amdgcn_sched_barrier(0x0006);
   };
-  auto convert = [&](int slot) {
+  // Codes of slot `slot` -> converted operands of slot `fs`.
+  auto convert = [&](int slot, int fs) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      fa[mt][0] = cvt8(qa[slot][mt].x, qa[slot][mt].y);
-      fa[mt][1] = cvt8(qa[slot][mt].z, qa[slot][mt].w);
+      fa[fs][mt][0] = cvt8(qa[slot][mt].x, qa[slot][mt].y);
+      fa[fs][mt][1] = cvt8(qa[slot][mt].z, qa[slot][mt].w);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      fb[nt][0] = cvt8(qb[slot][nt].x, qb[slot][nt].y);
-      fb[nt][1] = cvt8(qb[slot][nt].z, qb[slot][nt].w);
+      fb[fs][nt][0] = cvt8(qb[slot][nt].x, qb[slot][nt].y);
+      fb[fs][nt][1] = cvt8(qb[slot][nt].z, qb[slot][nt].w);
     }
   };
-  auto multiply = [&]() {
+  auto multiply = [&](int fs) {
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          p[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[nt][k], fa[mt][k], p[mt][nt], 0, 0, 0);
+          p[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[fs][nt][k], fa[fs][mt][k], p[mt][nt], 0, 0, 0);
   };
 
-  // Block lb from `cur` (its slice 0 already in registers).  Slices 1..3 are
-  // read one ahead of the multiply.  Once the last slice is in registers the
-  // wave waits for its share of block lb + 1, the workgroup synchronises,
-  // `cur` is refilled with block lb + NS and slice 0 of block lb + 1 is read
-  // from `nxt` -- all while the last slice is multiplied (its MFMAs issued
-  // before the barrier with 8 waves, after the refill issue with 4).  The
-  // block's scales are read into registers before `cur` can be refilled.
+  // Block lb from `cur`.
+  // Two schedules.  With 8 waves (two per SIMD) and block scales of B (the
+  // forward and data-gradient GEMMs): on entry slice 0 is converted (operand
+  // slot 0)
+  // and the codes of slice 1 are read (code slot 1).  Each slice's MFMAs use
+  // operands converted during the slice before, while the next slice is
+  // converted and the one after it read, so a wave's MFMAs never wait for its
+  // own conversions.  Slices 2 and 3 are multiplied before the block-end
+  // barrier (they run while the wave waits there for the slowest wave); after
+  // it `cur` is refilled with block lb + NS, slices 0 and 1 of block lb + 1 are
+  // read from `nxt` and slice 0 is converted.
+  // Otherwise one operand slot: slice 0 is read on entry, slices 1..3 are
+  // read one ahead of the multiply, each converted just before it; with 8
+  // waves slice 3 is multiplied before the barrier, with 4 after it, once
+  // `cur` is refilled and slice 0 of block lb + 1 is read.  (The second slot
+  // was measured: 2% faster on the forward and data-gradient GEMMs, 4% slower
+  // on the 8-wave weight gradients, which then need 254 registers; the 4-wave
+  // tiles, two workgroups per CU, spill with it.)
+  // The block's scales are read into registers before `cur` can be refilled.
   auto step = [&](uint8_t* cur, const uint8_t* nxt, int lb) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) p[mt][nt] = v16f{};
-#pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      load_slice(cur, c + 1, (c + 1) & 1);
-      convert(c & 1);
-      multiply();
-    }
-    convert(1);
-    // With 8 waves (two per SIMD) the last slice's MFMAs are issued before the
-    // block-end barrier, so that they run while the wave waits there for the
-    // slowest wave; with 4 waves they follow the refill issue (measured: +2-3%
-    // on the 256 x 128 tiles' GEMMs, -2-4% on the 128 x 128 ones).
-    if (NW == 8) {
-      multiply();
+    if constexpr (kAhead) {
+      load_slice(cur, 2, 0);
+      convert(1, 1);
+      multiply(0);
+      load_slice(cur, 3, 1);
+      convert(0, 0);
+      multiply(1);
+      convert(1, 1);
+      multiply(0);
+      multiply(1);
       __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        load_slice(cur, c + 1, (c + 1) & 1);
+        convert(c & 1, 0);
+        multiply(0);
+      }
+      convert(1, 0);
+      if (NW == 8) {
+        multiply(0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     const float* lsa = reinterpret_cast<const float*>(cur + C::kSaOff);
     float sa[MT];                  // A scale of this lane's output row
@@ -520,8 +544,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
     if (lb + NS < nLB) stage_all(lb + NS, cur);
-    if (lb + 1 < nLB) load_slice(nxt, 0, 0);
-    if (NW != 8) multiply();
+    if constexpr (kAhead) {
+      if (lb + 1 < nLB) {
+        load_slice(nxt, 0, 0);
+        load_slice(nxt, 1, 1);
+        convert(0, 0);
+      }
+    } else {
+      if (lb + 1 < nLB) load_slice(nxt, 0, 0);
+      if (NW != 8) multiply(0);
+    }
     float4 sbr[NT][4];             // SB_ROWS: B scales of output columns 8q + 4h + u
     const float* lsb = sb_ring + (lb % C::kRing) * BN;
 #pragma unroll
@@ -561,6 +593,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && NS == 2) ? 2 : 1) void block_g
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
   load_slice(lds0, 0, 0);
+  if (kAhead) {
+    load_slice(lds0, 1, 1);
+    convert(0, 0);
+  }
   if (NS == 2) {
     for (int lb = 0; lb < nLB; lb += 2) {
       step(lds0, lds1, lb);
