@@ -310,6 +310,29 @@ def test_two_k_groups_unsplit(B, M, N, K):
     assert ok, f"wgrad accumulate {M}x{N}x{K}: {rep}"
 
 
+@pytest.mark.parametrize("nblk", [1, 2, 3])
+def test_big_tiles_short_contractions(B, nblk):
+    """256 x 128 tiles (one full round: 16 x 16 tiles over 4000 ragged rows) with
+    contractions of 1, 2 and 3 scale blocks, where the software pipeline's
+    prologue and its last-block guards decide what is read and converted: the
+    forward GEMM (K = 128 nblk) in BF16 and the data gradient (N = 128 nblk) in
+    FP32, every element against the oracle."""
+    torch = _torch()
+    M, D = 4000, 2048
+    for lin, (name, N, K) in enumerate((("fwd", D, 128 * nblk), ("dgrad", 128 * nblk, D))):
+        xb = W.normal_bf16((M, K), 1.0, W.seed_for(98, nblk, lin, "x"))
+        wb = W.normal_bf16((N, K), 0.02, W.seed_for(98, nblk, lin, "w"))
+        dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(98, nblk, lin, "dy"))
+        L = Layer(B, xb, wb, dyb)
+        say("gemm big tiles", name, (M, N, K))
+        if name == "fwd":
+            got, ref = L.fwd(torch.bfloat16)
+            check_full(got, ref, "bf16", f"fwd {M}x{N}x{K}")
+        else:
+            got, ref = L.dgrad(torch.float32)
+            check_full(got, ref, "f32", f"dgrad {M}x{N}x{K}")
+
+
 def test_determinism(B):
     torch = _torch()
     xb = W.normal_bf16((512, 1024), 1.0, 8)
