@@ -312,11 +312,13 @@ def test_two_k_groups_unsplit(B, M, N, K):
 
 @pytest.mark.parametrize("nblk", [1, 2, 3])
 def test_big_tiles_short_contractions(B, nblk):
-    """256 x 128 tiles (one full round: 16 x 16 tiles over 4000 ragged rows) with
-    contractions of 1, 2 and 3 scale blocks, where the software pipeline's
-    prologue and its last-block guards decide what is read and converted: the
-    forward GEMM (K = 128 nblk) in BF16 and the data gradient (N = 128 nblk) in
-    FP32, every element against the oracle."""
+    """256 x 128 tiles (one full round of 16 x 16 tiles) with contractions of 1,
+    2 and 3 scale blocks, where the software pipeline's prologue and its
+    last-block guards decide what is read and converted: the forward GEMM
+    (K = 128 nblk) in BF16 and the data gradient (N = 128 nblk) in FP32 over
+    4000 ragged rows, and the weight gradient of a 4096 x 2048 weight over
+    128 nblk - 28 tokens (a ragged last token group), every element against the
+    oracle."""
     torch = _torch()
     M, D = 4000, 2048
     for lin, (name, N, K) in enumerate((("fwd", D, 128 * nblk), ("dgrad", 128 * nblk, D))):
@@ -331,6 +333,13 @@ def test_big_tiles_short_contractions(B, nblk):
         else:
             got, ref = L.dgrad(torch.float32)
             check_full(got, ref, "f32", f"dgrad {M}x{N}x{K}")
+    T, N, K = 128 * nblk - 28, 4096, D
+    xb = W.normal_bf16((T, K), 1.0, W.seed_for(98, nblk, 2, "x"))
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(98, nblk, 2, "w"))
+    dyb = W.normal_bf16((T, N), 1e-3, W.seed_for(98, nblk, 2, "dy"))
+    say("gemm big tiles wgrad", (T, N, K))
+    got, ref = Layer(B, xb, wb, dyb).wgrad()
+    check_full(got, ref, "f32", f"wgrad {N}x{K} over {T}")
 
 
 def test_determinism(B):
