@@ -461,6 +461,30 @@ def test_fp8_matrix_core_small_gaussian(B, M, N, K):
     assert ok, f"fp8 wgrad accumulate: {rep}"
 
 
+@pytest.mark.parametrize("nblk", [1, 3])
+def test_fp8_matrix_core_big_tiles_short_contractions(B, nblk):
+    """The FP8 matrix path on 256 x 128 tiles with contractions of 1 and 3 scale
+    blocks (forward and data gradient over 4000 ragged rows, weight gradient over
+    128 nblk - 28 tokens), every element against the derived bound."""
+    torch = _torch()
+    M, D = 4000, 2048
+    for lin, (name, N, K) in enumerate((("fwd", D, 128 * nblk), ("dgrad", 128 * nblk, D))):
+        xb = W.normal_bf16((M, K), 1.0, W.seed_for(99, nblk, lin, "x"))
+        wb = W.normal_bf16((N, K), 0.02, W.seed_for(99, nblk, lin, "w"))
+        dyb = W.normal_bf16((M, N), 1e-3, W.seed_for(99, nblk, lin, "dy"))
+        L = FastLayer(B, xb, wb, dyb)
+        say("fp8 path big tiles", name, (M, N, K))
+        got, ref = (L.fwd if name == "fwd" else L.dgrad)(torch.float32)
+        _check_fp32_rtol(got, ref, FP8_PATH_RTOL, f"fp8 {name} {M}x{N}x{K}")
+    T, N, K = 128 * nblk - 28, 4096, D
+    xb = W.normal_bf16((T, K), 1.0, W.seed_for(99, nblk, 2, "x"))
+    wb = W.normal_bf16((N, K), 0.02, W.seed_for(99, nblk, 2, "w"))
+    dyb = W.normal_bf16((T, N), 1e-3, W.seed_for(99, nblk, 2, "dy"))
+    say("fp8 path big tiles wgrad", (T, N, K))
+    got, ref = FastLayer(B, xb, wb, dyb).wgrad()
+    _check_fp32_rtol(got, ref, FP8_PATH_RTOL, f"fp8 wgrad {N}x{K} over {T}")
+
+
 def test_fp8_matrix_core_config1_exact_tolerance(B):
     """On configuration 1 (Gaussian) the FP8 path also meets the exact-block tolerance."""
     torch = _torch()
